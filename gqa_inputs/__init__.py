@@ -1,0 +1,161 @@
+"""Seeded synthetic inputs for grouped-query attention.
+
+This module only draws random tensors and builds sequence offsets. It holds
+none of the attention arithmetic, so both the fp64 oracle (``oracle/``) and
+the HIP path (``gqa_attention_amd``) can take their inputs from it without
+sharing any computation.
+
+Recipe (every tensor is i.i.d. N(0, 1)):
+
+* one ``torch.Generator('cpu')`` per workload, seeded with the workload's seed;
+* draws happen in the order q, k, v (variable-length workloads draw the
+  sequence lengths first);
+* fp32 is drawn, then bf16 workloads are rounded to bf16 with round-to-nearest
+  even (``.to(torch.bfloat16)``); the oracle reads those same bf16 values
+  upcast to fp64.
+
+Layouts: fixed length ``[B, S, H, d]`` (batch, sequence, head, head_dim);
+variable length ``[T, H, d]`` with int32 ``cu_seqlens`` of length B+1;
+decode ``q [B, Hq, d]`` with a cache ``[B, Sk, Hkv, d]``.
+
+The five named workloads take their shapes from the pages: the GQA snippet of
+the Ultralytics glossary page "Grouped Query Attention (GQA)" (8 query heads,
+2 KV heads, 16 tokens, head_dim 64), a BERT-base encoder (12 heads, d 64,
+sequence 512, batch 64) from the gitcode GQA batch-size guide's A100 BERT
+table, Llama 3.1 8B (32 query heads, 8 KV heads, d 128) from the glossary's
+KV-cache section, the 48/12 (4:1) grouping from the guide's KV-memory
+paragraph, and variable-length packed inputs from the Raptor-T abstract.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+
+@dataclass
+class Workload:
+    """One seeded input set. Tensors live on the CPU; callers copy them."""
+
+    name: str
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    causal: bool
+    scale: float
+    cu_seqlens_q: Optional[torch.Tensor] = None  # int32 [B+1]
+    cu_seqlens_k: Optional[torch.Tensor] = None
+    max_seqlen_q: Optional[int] = None
+    max_seqlen_k: Optional[int] = None
+    decode: bool = False
+
+    @property
+    def varlen(self) -> bool:
+        return self.cu_seqlens_q is not None
+
+
+def _randn(g: torch.Generator, shape, dtype: torch.dtype) -> torch.Tensor:
+    x = torch.randn(*shape, dtype=torch.float32, generator=g)
+    return x.to(dtype) if dtype != torch.float32 else x
+
+
+def fixed(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int, *, seed: int,
+          dtype: torch.dtype = torch.bfloat16, causal: bool = False,
+          scale: Optional[float] = None, name: str = "fixed") -> Workload:
+    """Fixed-length q [B, Sq, Hq, d], k/v [B, Sk, Hkv, d]."""
+    g = torch.Generator().manual_seed(seed)
+    q = _randn(g, (B, Sq, Hq, d), dtype)
+    k = _randn(g, (B, Sk, Hkv, d), dtype)
+    v = _randn(g, (B, Sk, Hkv, d), dtype)
+    return Workload(name, q, k, v, causal, d ** -0.5 if scale is None else scale)
+
+
+def varlen(lengths_q, lengths_k, Hq: int, Hkv: int, d: int, *, seed: int,
+           dtype: torch.dtype = torch.bfloat16, causal: bool = False,
+           scale: Optional[float] = None, name: str = "varlen") -> Workload:
+    """Packed q [sum Lq, Hq, d], k/v [sum Lk, Hkv, d] with int32 cu_seqlens."""
+    lq = [int(x) for x in lengths_q]
+    lk = [int(x) for x in lengths_k]
+    g = torch.Generator().manual_seed(seed)
+    q = _randn(g, (sum(lq), Hq, d), dtype)
+    k = _randn(g, (sum(lk), Hkv, d), dtype)
+    v = _randn(g, (sum(lk), Hkv, d), dtype)
+    cq = torch.tensor([0] + lq, dtype=torch.int64).cumsum(0).to(torch.int32)
+    ck = torch.tensor([0] + lk, dtype=torch.int64).cumsum(0).to(torch.int32)
+    return Workload(name, q, k, v, causal, d ** -0.5 if scale is None else scale,
+                    cq, ck, max(lq) if lq else 0, max(lk) if lk else 0)
+
+
+def decode(B: int, Hq: int, Hkv: int, Sk: int, d: int, *, seed: int,
+           dtype: torch.dtype = torch.bfloat16, scale: Optional[float] = None,
+           name: str = "decode") -> Workload:
+    """One new token per sequence: q [B, Hq, d]; cache k/v [B, Sk, Hkv, d]."""
+    g = torch.Generator().manual_seed(seed)
+    q = _randn(g, (B, Hq, d), dtype)
+    k = _randn(g, (B, Sk, Hkv, d), dtype)
+    v = _randn(g, (B, Sk, Hkv, d), dtype)
+    return Workload(name, q, k, v, False, d ** -0.5 if scale is None else scale,
+                    decode=True)
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads.
+# ---------------------------------------------------------------------------
+
+def tiny_causal_gqa_fp32() -> Workload:
+    """8 query heads, 2 KV heads, 16 tokens, d 64, causal, fp32.
+
+    Drawn exactly as the glossary snippet draws them: seed 0, then
+    randn(1, 8, 16, 64) for q and randn(1, 2, 16, 64) for k and v in the
+    [batch, heads, seq, d] layout; transposed here to [batch, seq, heads, d].
+    """
+    g = torch.Generator().manual_seed(0)
+    q = torch.randn(1, 8, 16, 64, generator=g)
+    k = torch.randn(1, 2, 16, 64, generator=g)
+    v = torch.randn(1, 2, 16, 64, generator=g)
+    t = lambda x: x.transpose(1, 2).contiguous()
+    return Workload("tiny_causal_gqa_fp32", t(q), t(k), t(v), True, 64 ** -0.5)
+
+
+def bert_base_encoder() -> Workload:
+    """Non-causal MHA: B 64, S 512, 12 heads, d 64, bf16 (seed 2)."""
+    return fixed(64, 12, 12, 512, 512, 64, seed=2, causal=False,
+                 name="bert_base_encoder_b64_s512_h12_d64")
+
+
+def llama31_8b_prefill() -> Workload:
+    """Causal GQA prefill: B 1, S 8192, 32 query / 8 KV heads, d 128, bf16 (seed 3)."""
+    return fixed(1, 32, 8, 8192, 8192, 128, seed=3, causal=True,
+                 name="llama31_8b_prefill_s8192_h32_kv8_d128")
+
+
+def llama31_8b_decode() -> Workload:
+    """Decode: B 64, 32 query / 8 KV heads, d 128, 4096-token cache, bf16 (seed 4)."""
+    return decode(64, 32, 8, 4096, 128, seed=4,
+                  name="llama31_8b_decode_b64_kv4096_h32_kv8_d128")
+
+
+def varlen_packed_causal_48_12() -> Workload:
+    """Packed causal GQA 4:1: 48 query / 12 KV heads, d 128, 32 sequences.
+
+    Lengths are drawn first, uniform on [128, 4096] from seed 5.
+    """
+    g = torch.Generator().manual_seed(5)
+    lengths = torch.randint(128, 4097, (32,), generator=g).tolist()
+    T = sum(lengths)
+    q = _randn(g, (T, 48, 128), torch.bfloat16)
+    k = _randn(g, (T, 12, 128), torch.bfloat16)
+    v = _randn(g, (T, 12, 128), torch.bfloat16)
+    cu = torch.tensor([0] + lengths, dtype=torch.int64).cumsum(0).to(torch.int32)
+    return Workload("varlen_packed_causal_h48_kv12_d128_n32", q, k, v, True,
+                    128 ** -0.5, cu, cu.clone(), max(lengths), max(lengths))
+
+
+NAMED = {
+    "tiny_causal_gqa_fp32": tiny_causal_gqa_fp32,
+    "bert_base_encoder": bert_base_encoder,
+    "llama31_8b_prefill": llama31_8b_prefill,
+    "llama31_8b_decode": llama31_8b_decode,
+    "varlen_packed_causal": varlen_packed_causal_48_12,
+}

@@ -1,0 +1,15 @@
+"""fp64 CPU oracle for grouped-query attention.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the smoke check in
+``__graft_entry__.py`` and by the CPU-baseline leg of ``bench.py``, never by
+the ``gqa_attention_amd`` package. It shares no code with the HIP path.
+
+Modules:
+  gqa        the plain definition (materialised S and P, K/V expanded per head)
+  brute      a pure-Python scalar restatement used to pin ``attention``
+  kv_cache   KV-cache size arithmetic pinned to the glossary's printed figures
+"""
+from .gqa import (attention, attention_rows, decode, decode_partials,  # noqa: F401
+                        merge_partials, split_ranges, attention_flops, head_rows,
+                        expand_kv, kv_head_of, visible, as_f64)
+from .kv_cache import kv_cache_bytes, kv_cache_elements  # noqa: F401
