@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused GQA attention forward / split-KV decode on one MI355X.
+
+Default run (N = 1): the BERT-base encoder workload (B 64, S 512, 12 heads,
+d 64, non-causal, bf16) through ``gqa_attn_fwd``; one step = one forward over
+the batch with inputs already resident in HBM. Three input sets are rotated
+so consecutive launches never hit the same buffers (the set of one launch fits
+the 256 MB Infinity Cache; three do not).
+
+Printed: ONE JSON line with the metric, the dominant kernel's roofline
+(algorithmic flops or bytes per launch / launch time from HIP events on the
+launch stream), the CPU oracle timed on a bounded sample (rank 0, N = 1) and,
+under "extra", the other workloads (8192-token causal GQA prefill, split-KV
+decode at num_splits 1/2/4/8, packed variable-length causal GQA, tiny fp32).
+
+Flop count: 4 * d per visible (query, key) pair per query head (two products,
+multiply-add = 2 flops). Decode bytes: the K and V cache bytes read,
+2 * B * Sk * Hkv * d * 2.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
+METRIC = "fwd attention TFLOP/s (% MFMA peak); decode KV GB/s (% HBM peak)"
+
+
+def fwd_flops(lq: int, lk: int, hq: int, d: int, causal: bool) -> int:
+    """Algorithmic flops of one sequence (4 d per visible pair per query head)."""
+    if not causal:
+        return 4 * d * hq * lq * lk
+    shift = lk - lq
+    pairs = 0
+    # visible keys of row i: min(lk, max(0, i + 1 + shift))
+    lo = max(0, -shift)            # first row with >= 1 visible key
+    hi = min(lq, lk - shift)       # rows before hi see fewer than lk keys
+    if hi > lo:
+        a, b = lo + 1 + shift, hi + shift  # arithmetic series of visible counts
+        pairs += (a + b) * (hi - lo) // 2
+    pairs += max(0, lq - max(hi, lo)) * lk if lk > 0 else 0
+    return 4 * d * hq * pairs
+
+
+def source_digest(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "fwd_bf16": ["gqa_attention_amd/csrc/fwd_bf16.hip", "gqa_attention_amd/csrc/device_util.h"],
+    "decode_bf16": ["gqa_attention_amd/csrc/decode_bf16.hip",
+                    "gqa_attention_amd/csrc/device_util.h"],
+}
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{kernel}:{workload}")
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_digest") != source_digest(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Timer:
+    """Per-launch HIP-event timing on the launch stream."""
+
+    def __init__(self, torch, n):
+        self.torch = torch
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+
+    def avg_ms(self):
+        ts = [a.elapsed_time(b) for a, b in self.ev]
+        return sum(ts) / len(ts), min(ts)
+
+
+def run_timed(torch, step, steps, warmup):
+    """W untimed steps, then exactly K timed steps between two synchronisations."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    tm = Timer(torch, steps)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        a, b = tm.ev[i]
+        a.record()
+        step(i)
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg, mn = tm.avg_ms()
+    return wall, avg, mn
+
+
+def to_device(torch, w, sets):
+    import gqa_inputs  # noqa: F401
+    out = []
+    for s in range(sets):
+        if s == 0:
+            q, k, v = w.q, w.k, w.v
+        else:  # further sets: same distribution, different draws
+            g = torch.Generator().manual_seed(10_000 + s)
+            q = torch.randn(w.q.shape, generator=g).to(w.q.dtype)
+            k = torch.randn(w.k.shape, generator=g).to(w.k.dtype)
+            v = torch.randn(w.v.shape, generator=g).to(w.v.dtype)
+        out.append((q.cuda(), k.cuda(), v.cuda()))
+    return out
+
+
+def bench_fwd(torch, ga, w, steps, warmup, sets):
+    dev_sets = to_device(torch, w, sets)
+    cq = w.cu_seqlens_q.cuda() if w.varlen else None
+    ck = w.cu_seqlens_k.cuda() if w.varlen else None
+    outs = [(torch.empty_like(q), None) for q, _, _ in dev_sets]
+    lses = []
+    for q, _, _ in dev_sets:
+        shape = (q.shape[0], q.shape[1]) if w.varlen else (q.shape[0], q.shape[2], q.shape[1])
+        lses.append(torch.empty(shape, dtype=torch.float32, device="cuda"))
+
+    def step(i):
+        j = i % sets
+        q, k, v = dev_sets[j]
+        if w.varlen:
+            ga.fwd(q, k, v, causal=w.causal, scale=w.scale, cu_seqlens_q=cq, cu_seqlens_k=ck,
+                   max_seqlen_q=w.max_seqlen_q, max_seqlen_k=w.max_seqlen_k, out=outs[j][0],
+                   lse=lses[j])
+        else:
+            ga.fwd(q, k, v, causal=w.causal, scale=w.scale, out=outs[j][0], lse=lses[j])
+
+    wall, avg_ms, min_ms = run_timed(torch, step, steps, warmup)
+    if w.varlen:
+        cu = w.cu_seqlens_q.tolist()
+        flops = sum(fwd_flops(cu[b + 1] - cu[b], cu[b + 1] - cu[b], w.q.shape[1], w.q.shape[2],
+                              w.causal) for b in range(len(cu) - 1))
+    else:
+        B, S, H, d = w.q.shape
+        flops = B * fwd_flops(S, w.k.shape[1], H, d, w.causal)
+    return dict(flops=flops, wall=wall, avg_ms=avg_ms, min_ms=min_ms)
+
+
+def bench_decode(torch, ga, w, ns, steps, warmup, sets):
+    dev_sets = to_device(torch, w, sets)
+    B, Hq, d = w.q.shape
+    out = torch.empty_like(dev_sets[0][0])
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, ga.decode_workspace_bytes(B, Hq, d, ns)), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(i):
+        q, k, v = dev_sets[i % sets]
+        ga.decode(q, k, v, scale=w.scale, num_splits=ns, workspace=ws, out=out, lse=lse)
+
+    wall, avg_ms, min_ms = run_timed(torch, step, steps, warmup)
+    kv_bytes = 2 * w.k.numel() * w.k.element_size()
+    return dict(bytes=kv_bytes, wall=wall, avg_ms=avg_ms, min_ms=min_ms)
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The fp64 oracle as it stands, on the first batches of the workload until
+    about `budget_s` seconds of CPU work; reported in the metric's unit."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    B = w.q.shape[0]
+    done, flops = 0, 0
+    t0 = time.perf_counter()
+    while done < B and (time.perf_counter() - t0) < budget_s:
+        oracle.attention(w.q[done:done + 1], w.k[done:done + 1], w.v[done:done + 1], w.scale,
+                         w.causal)
+        flops += fwd_flops(w.q.shape[1], w.k.shape[1], w.q.shape[2], w.q.shape[3], w.causal)
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {B} sequences (all {w.q.shape[2]} heads each), fp64 NumPy, "
+                      f"{el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="bert_base_encoder",
+                    choices=["bert_base_encoder", "llama31_8b_prefill", "llama31_8b_decode",
+                             "varlen_packed_causal", "tiny_causal_gqa_fp32"])
+    ap.add_argument("--num-splits", type=int, default=1, help="decode workload only")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gqa_attention_amd as ga
+    import gqa_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ga.lib()  # fail loudly if the HIP library is missing
+
+    def fwd_entry(name, w, steps, warmup, sets):
+        r = bench_fwd(torch, ga, w, steps, warmup, sets)
+        tf = r["flops"] / (r["avg_ms"] * 1e-3) / 1e12
+        peak = PEAK_BF16_TFLOPS if w.q.dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
+        return r, {"workload": w.name, "kernel": "fwd_bf16" if w.q.dtype == torch.bfloat16
+                   else "fwd_f32", "tflops": round(tf, 2), "frac_peak": round(tf / peak, 4),
+                   "ms_per_launch": round(r["avg_ms"], 5), "min_ms": round(r["min_ms"], 5),
+                   "gflop": round(r["flops"] / 1e9, 3)}
+
+    loaders = {
+        "bert_base_encoder": gqa_inputs.bert_base_encoder,
+        "llama31_8b_prefill": gqa_inputs.llama31_8b_prefill,
+        "varlen_packed_causal": gqa_inputs.varlen_packed_causal_48_12,
+        "tiny_causal_gqa_fp32": gqa_inputs.tiny_causal_gqa_fp32,
+        "llama31_8b_decode": gqa_inputs.llama31_8b_decode,
+    }
+    sets_for = {"bert_base_encoder": 3, "llama31_8b_decode": 2}
+
+    w = loaders[args.workload]()
+    sets = sets_for.get(args.workload, 1)
+    if w.decode:
+        r = bench_decode(torch, ga, w, args.num_splits, args.steps, args.warmup, sets)
+        gbs = r["bytes"] / (r["avg_ms"] * 1e-3) / 1e9
+        value = r["bytes"] * args.steps / r["wall"] / 1e9
+        unit, dtype_s = "GB/s", "bf16"
+        kernel = "decode_bf16"
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        traffic = measured_traffic(kernel, w.name)
+        config = {"workload": w.name, "B": w.q.shape[0], "Hq": w.q.shape[1], "Hkv": w.k.shape[2],
+                  "Sk": w.k.shape[1], "d": w.q.shape[2], "num_splits": args.num_splits,
+                  "kv_bytes": r["bytes"], "input_sets_rotated": sets}
+    else:
+        r = bench_fwd(torch, ga, w, args.steps, args.warmup, sets)
+        tf = r["flops"] / (r["avg_ms"] * 1e-3) / 1e12
+        value = r["flops"] * args.steps / r["wall"] / 1e12
+        unit = "TFLOP/s"
+        bf16 = w.q.dtype == torch.bfloat16
+        dtype_s = "bf16" if bf16 else "f32"
+        kernel = "fwd_bf16" if bf16 else "fwd_f32"
+        peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
+        roof = {"bound": "mfma" if bf16 else "alu", "achieved": round(tf, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(tf / peak, 4)}
+        traffic = measured_traffic(kernel, w.name) if bf16 else None
+        if w.varlen:
+            config = {"workload": w.name, "sequences": len(w.cu_seqlens_q) - 1,
+                      "total_tokens": w.q.shape[0], "Hq": w.q.shape[1], "Hkv": w.k.shape[1],
+                      "d": w.q.shape[2], "causal": w.causal}
+        else:
+            config = {"workload": w.name, "B": w.q.shape[0], "Sq": w.q.shape[1],
+                      "Sk": w.k.shape[1], "Hq": w.q.shape[2], "Hkv": w.k.shape[2],
+                      "d": w.q.shape[3], "causal": w.causal}
+        config["gflop_per_step"] = round(r["flops"] / 1e9, 3)
+        config["input_sets_rotated"] = sets
+    roof["traffic"] = traffic
+    roof["kernel"] = kernel
+    roof["launch_ms"] = round(r["avg_ms"], 5)
+
+    line = {"metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(r["wall"] * 1e3 / args.steps, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype_s, "data": "synthetic",
+            "config": config, "roofline": roof}
+
+    if not args.no_extra:
+        extra = []
+        for name in ["llama31_8b_prefill", "varlen_packed_causal", "tiny_causal_gqa_fp32",
+                     "bert_base_encoder"]:
+            if name == args.workload:
+                continue
+            wx = loaders[name]()
+            _, e = fwd_entry(name, wx, 20, 3, sets_for.get(name, 1))
+            extra.append(e)
+            del wx
+        if args.workload != "llama31_8b_decode":
+            wd = loaders["llama31_8b_decode"]()
+            for ns in (1, 2, 4, 8):
+                rd = bench_decode(torch, ga, wd, ns, 20, 3, 2)
+                gbs = rd["bytes"] / (rd["avg_ms"] * 1e-3) / 1e9
+                extra.append({"workload": wd.name, "kernel": "decode_bf16+combine" if ns > 1
+                              else "decode_bf16", "num_splits": ns, "kv_gbs": round(gbs, 1),
+                              "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
+                              "ms_per_call": round(rd["avg_ms"], 5)})
+            del wd
+        line["extra"] = extra
+
+    if not args.no_cpu_baseline and not w.decode:
+        line["cpu_baseline"] = cpu_baseline(w)
+    elif not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        nb = 0
+        while nb < w.q.shape[0] and time.perf_counter() - t0 < 15.0:
+            oracle.decode(w.q[nb:nb + 1], w.k[nb:nb + 1], w.v[nb:nb + 1], w.scale)
+            nb += 1
+        el = time.perf_counter() - t0
+        kvb = 2 * w.k[:nb].numel() * w.k.element_size()
+        line["cpu_baseline"] = {"value": kvb / el / 1e9, "unit": "GB/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": f"{nb} of {w.q.shape[0]} sequences, fp64 NumPy, {el:.1f} s"}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,225 @@
+"""Python binding of libgqa_attn.so (argument marshalling only).
+
+Every step of the attention computation runs in the HIP kernels behind the C
+ABI declared in ``include/gqa_attn.h``; this module only checks tensor
+metadata, allocates outputs with ``torch.empty`` on the tensors' device, and
+passes raw device pointers plus the current HIP stream. There is no CPU
+fallback: if the library is missing, importing works but every call raises.
+
+Functions mirror the C entry points:
+
+* ``fwd(q, k, v, causal=False, scale=None, cu_seqlens_q=None, cu_seqlens_k=None,
+  max_seqlen_q=None, max_seqlen_k=None)`` -> ``(out, lse)``
+* ``decode(q, k_cache, v_cache, scale=None, num_splits=1, workspace=None)`` ->
+  ``(out, lse)``
+* ``decode_workspace_bytes(B, Hq, d, num_splits)``
+* ``strerror(status)``
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["fwd", "decode", "decode_workspace_bytes", "strerror", "lib", "library_path",
+           "GQA_OK", "GQA_EINVAL", "GQA_EUNSUPPORTED", "GQA_EWORKSPACE", "GQA_ELAUNCH",
+           "GQA_DTYPE_BF16", "GQA_DTYPE_FP32", "GqaError"]
+
+GQA_OK, GQA_EINVAL, GQA_EUNSUPPORTED, GQA_EWORKSPACE, GQA_ELAUNCH = 0, 1, 2, 3, 4
+GQA_DTYPE_BF16, GQA_DTYPE_FP32 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgqa_attn.so")
+_lib = None
+
+
+class GqaError(RuntimeError):
+    """A non-zero status from the C ABI."""
+
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m gqa_attention_amd.build` "
+            "(there is no fallback implementation)")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.gqa_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
+                               vp, vp, i32, vp]
+    L.gqa_attn_fwd.restype = i32
+    L.gqa_attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz,
+                                  i32, vp]
+    L.gqa_attn_decode.restype = i32
+    L.gqa_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.gqa_attn_decode_workspace_bytes.restype = sz
+    L.gqa_attn_strerror.argtypes = [i32]
+    L.gqa_attn_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    return lib().gqa_attn_strerror(int(status)).decode()
+
+
+def _raise(status: int, where: str):
+    if status == GQA_OK:
+        return
+    if status == GQA_ELAUNCH:
+        raise GqaError(status, where)
+    raise ValueError(f"{where}: {strerror(status)} (status {status})")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GQA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return GQA_DTYPE_FP32
+    raise ValueError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def _check(name: str, t: torch.Tensor, ndim: int, dtype: torch.dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+        scale: Optional[float] = None, cu_seqlens_q: Optional[torch.Tensor] = None,
+        cu_seqlens_k: Optional[torch.Tensor] = None, max_seqlen_q: Optional[int] = None,
+        max_seqlen_k: Optional[int] = None, out: Optional[torch.Tensor] = None,
+        lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Exact GQA attention forward through ``gqa_attn_fwd``.
+
+    Fixed length: q [B, Sq, Hq, d], k/v [B, Sk, Hkv, d] -> out like q,
+    lse fp32 [B, Hq, Sq]. Variable length: q [Tq, Hq, d], k/v [Tk, Hkv, d],
+    int32 cu_seqlens [B+1] on the device and the maximum lengths (which size
+    the grid; no host read of device data happens) -> lse fp32 [Tq, Hq].
+    ``scale`` defaults to 1/sqrt(d).
+    """
+    dt = q.dtype
+    varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
+    nd = 3 if varlen else 4
+    dev = q.device
+    _check("q", q, nd, dt, None)
+    _check("k", k, nd, dt, dev)
+    _check("v", v, nd, dt, dev)
+    code = _dtype_code(q)
+    d = q.shape[-1]
+    if k.shape[-1] != d or v.shape[-1] != d or k.shape != v.shape:
+        raise ValueError("q, k, v head_dim and k/v shapes must agree")
+    Hq, Hkv = q.shape[-2], k.shape[-2]
+    if varlen:
+        if cu_seqlens_q is None or cu_seqlens_k is None:
+            raise ValueError("give both cu_seqlens_q and cu_seqlens_k")
+        _check("cu_seqlens_q", cu_seqlens_q, 1, torch.int32, dev)
+        _check("cu_seqlens_k", cu_seqlens_k, 1, torch.int32, dev)
+        if cu_seqlens_q.shape != cu_seqlens_k.shape:
+            raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+        if max_seqlen_q is None or max_seqlen_k is None:
+            raise ValueError("variable length needs max_seqlen_q and max_seqlen_k")
+        B = cu_seqlens_q.shape[0] - 1
+        Sq, Sk = int(max_seqlen_q), int(max_seqlen_k)
+        lse_shape = (q.shape[0], Hq)
+        cq, ck = cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr()
+    else:
+        B, Sq = q.shape[0], q.shape[1]
+        Sk = k.shape[1]
+        if k.shape[0] != B:
+            raise ValueError("q and k/v batch sizes differ")
+        lse_shape = (B, Hq, Sq)
+        cq = ck = None
+    if out is None:
+        out = torch.empty(q.shape, dtype=dt, device=dev)
+    else:
+        _check("out", out, nd, dt, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if lse is None:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=dev)
+    else:
+        _check("lse", lse, len(lse_shape), torch.float32, dev)
+        if tuple(lse.shape) != lse_shape:
+            raise ValueError(f"lse must have shape {lse_shape}")
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if q.numel() == 0:
+        return out, lse
+    with torch.cuda.device(dev):
+        st = lib().gqa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), B, Hq, Hkv, Sq, Sk, d, sc, int(bool(causal)),
+                                cq, ck, code, _stream_handle(dev))
+    _raise(st, "gqa_attn_fwd")
+    return out, lse
+
+
+def decode_workspace_bytes(B: int, Hq: int, d: int, num_splits: int) -> int:
+    return int(lib().gqa_attn_decode_workspace_bytes(B, Hq, d, num_splits))
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *,
+           scale: Optional[float] = None, num_splits: int = 1,
+           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-KV decode through ``gqa_attn_decode``.
+
+    q [B, Hq, d]; caches [B, Sk, Hkv, d] -> out [B, Hq, d], lse fp32 [B, Hq].
+    For num_splits > 1 a uint8 device workspace of
+    ``decode_workspace_bytes(B, Hq, d, num_splits)`` bytes is allocated unless
+    one is passed.
+    """
+    dt = q.dtype
+    dev = q.device
+    _check("q", q, 3, dt, None)
+    _check("k_cache", k_cache, 4, dt, dev)
+    _check("v_cache", v_cache, 4, dt, dev)
+    code = _dtype_code(q)
+    B, Hq, d = q.shape
+    if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[-1] != d:
+        raise ValueError("cache shapes must be [B, Sk, Hkv, d] matching q")
+    Sk, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if out is None:
+        out = torch.empty(q.shape, dtype=dt, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    _check("out", out, 3, dt, dev)
+    _check("lse", lse, 2, torch.float32, dev)
+    need = decode_workspace_bytes(B, Hq, d, num_splits) if num_splits >= 1 else 0
+    if num_splits > 1 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(dev):
+        st = lib().gqa_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                   out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Sk, d, sc,
+                                   int(num_splits), ws_ptr, ws_bytes, code, _stream_handle(dev))
+    _raise(st, "gqa_attn_decode")
+    return out, lse

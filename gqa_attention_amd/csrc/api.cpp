@@ -1,0 +1,161 @@
+// C ABI entry points: validate on the host, pick the kernel instance and the
+// grid, launch asynchronously on the caller's stream. Nothing here allocates,
+// synchronises or reads device memory.
+
+#include <cstdlib>
+#include <cstring>
+
+#include <hip/hip_runtime.h>
+
+#include "gqa_attn.h"
+#include "params.h"
+#include "validate.h"
+
+namespace gqa {
+int fwd_bf16_rows_per_tile();
+int fwd_f32_rows_per_tile();
+}  // namespace gqa
+
+namespace {
+
+// Debug knob for A/B measurements of query-head packing: GQA_ATTN_PACK=0
+// gives every query head its own row tiles (K/V then re-read per head).
+bool pack_enabled() {
+    static const bool on = [] {
+        const char *e = std::getenv("GQA_ATTN_PACK");
+        return !(e && std::strcmp(e, "0") == 0);
+    }();
+    return on;
+}
+
+int status_from(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char *gqa_attn_strerror(int status) {
+    switch (status) {
+        case GQA_OK: return "success";
+        case GQA_EINVAL: return "invalid argument";
+        case GQA_EUNSUPPORTED: return "unsupported head_dim or dtype";
+        case GQA_EWORKSPACE: return "decode workspace missing or too small";
+        case GQA_ELAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+size_t gqa_attn_decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
+    return gqa::decode_workspace_bytes(B, Hq, d, num_splits);
+}
+
+int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse, int B, int Hq,
+                 int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                 const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int dtype,
+                 void *stream) {
+    const int rc = gqa::validate_fwd(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, d, scale,
+                                     cu_seqlens_q, cu_seqlens_k, dtype);
+    if (rc != GQA_OK) return rc;
+    if (Sq == 0) return GQA_OK;  // variable length with no query rows at all
+
+    const bool varlen = cu_seqlens_q != nullptr;
+    gqa::FwdParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = out;
+    p.lse = lse;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Sq = Sq;
+    p.Sk = Sk;
+    p.G = Hq / Hkv;
+    p.gpack = pack_enabled() ? p.G : 1;
+    p.n_hg = B * (Hq / p.gpack);
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.num_splits = 1;
+    const int rows = dtype == GQA_DTYPE_BF16 ? gqa::fwd_bf16_rows_per_tile()
+                                             : gqa::fwd_f32_rows_per_tile();
+    p.n_rb = (int)(((long long)p.gpack * Sq + rows - 1) / rows);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (dtype == GQA_DTYPE_BF16)
+        return status_from(gqa::launch_fwd_bf16(p, d, causal != 0, varlen, s));
+    return status_from(gqa::launch_fwd_f32(p, d, causal != 0, varlen, false, s));
+}
+
+int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache, void *out,
+                    float *lse, int B, int Hq, int Hkv, int Sk, int d, float scale,
+                    int num_splits, void *workspace, size_t workspace_bytes, int dtype,
+                    void *stream) {
+    const int rc = gqa::validate_decode(q, k_cache, v_cache, out, lse, B, Hq, Hkv, Sk, d, scale,
+                                        num_splits, workspace, workspace_bytes, dtype);
+    if (rc != GQA_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int chunk = gqa::split_chunk(Sk, num_splits);
+    const int rows = B * Hq;
+    float *ws_o = nullptr, *ws_lse = nullptr;
+    if (num_splits > 1) {
+        size_t o_bytes = (size_t)num_splits * rows * d * sizeof(float);
+        o_bytes = (o_bytes + 255) & ~size_t(255);
+        ws_o = static_cast<float *>(workspace);
+        ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
+    }
+    (void)hipGetLastError();
+    if (dtype == GQA_DTYPE_BF16) {
+        gqa::DecodeParams p{};
+        p.q = q;
+        p.k = k_cache;
+        p.v = v_cache;
+        p.o = out;
+        p.lse = lse;
+        p.B = B;
+        p.Hq = Hq;
+        p.Hkv = Hkv;
+        p.Sk = Sk;
+        p.G = Hq / Hkv;
+        p.n_qs = (p.G + 15) / 16;
+        p.num_splits = num_splits;
+        p.split_chunk = chunk;
+        p.scale_log2 = scale * 1.4426950408889634f;
+        p.ws_o = ws_o;
+        p.ws_lse = ws_lse;
+        hipError_t e = gqa::launch_decode_bf16(p, d, s);
+        if (e != hipSuccess || num_splits == 1) return status_from(e);
+        return status_from(
+            gqa::launch_decode_combine(ws_o, ws_lse, out, lse, rows, num_splits, d, true, s));
+    }
+    // fp32: the fp32 forward kernel with one query position per sequence.
+    gqa::FwdParams p{};
+    p.q = q;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.o = out;
+    p.lse = lse;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Sq = 1;
+    p.Sk = Sk;
+    p.G = Hq / Hkv;
+    p.gpack = pack_enabled() ? p.G : 1;
+    p.n_hg = B * (Hq / p.gpack);
+    p.n_rb = (p.gpack + gqa::fwd_f32_rows_per_tile() - 1) / gqa::fwd_f32_rows_per_tile();
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    p.num_splits = num_splits;
+    p.split_chunk = chunk;
+    p.ws_o = ws_o;
+    p.ws_lse = ws_lse;
+    if (num_splits == 1) return status_from(gqa::launch_fwd_f32(p, d, false, false, false, s));
+    hipError_t e = gqa::launch_fwd_f32(p, d, false, false, true, s);
+    if (e != hipSuccess) return status_from(e);
+    return status_from(
+        gqa::launch_decode_combine(ws_o, ws_lse, out, lse, rows, num_splits, d, false, s));
+}
+
+}  // extern "C"

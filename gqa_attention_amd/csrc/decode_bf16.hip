@@ -1,0 +1,329 @@
+// Split-KV GQA decode (bf16) and the log-sum-exp combine of split partials.
+//
+// Decode: one new query token per sequence reads its whole K/V cache, so the
+// step is bound by HBM bandwidth (Ultralytics glossary, "How GQA shrinks the
+// KV cache"). The cache's key range is cut into num_splits contiguous ranges
+// (gitcode GQA guide, num_splits); each range gives a normalised partial
+// output O_s and its log-sum-exp L_s, and the partials are merged exactly
+// through L = M + log sum_s exp(L_s - M), O = sum_s exp(L_s - L) O_s (the
+// pages print no merge; this follows from the LSE definition on the
+// FlashAttention-2 page, L = m + log l).
+//
+// gfx950 mapping (our design):
+//  * workgroup = (batch, K/V head, split, slice of up to 16 query heads of
+//    the group): every K/V byte of the range is read from HBM exactly once
+//    and used by all G heads of the group (pack_gqa).
+//  * 4 wavefronts per workgroup, each streaming its own 32-key tiles (tiles
+//    w, w+4, ...) with its own running max / sum; the 4 partial states are
+//    merged through LDS at the end.
+//  * v_mfma_f32_16x16x32_bf16 for S^T = K Q^T (16 keys x 16 query heads) with
+//    K loaded from HBM straight into the A-operand layout, and for
+//    O^T = V^T P^T with V transposed through a wave-private LDS buffer. The
+//    next tile's loads are issued before the current tile's math.
+
+#include "device_util.h"
+#include "params.h"
+
+namespace gqa {
+
+namespace {
+
+constexpr int NTHREADS = 256;
+constexpr int NWAVES = 4;
+constexpr int TK = 32;        // keys per wave tile
+constexpr int VTS = TK + 4;   // LDS row stride of the wave's V^T tile (elements)
+
+template <int D>
+struct DecCfg {
+    static constexpr int NS = D / 32;    // k-steps of 32 head_dim elements
+    static constexpr int NDT = D / 16;   // 16-row tiles of O^T
+    static constexpr int NVB = D / 64;   // 4-key x 8-d V blocks per lane
+    static constexpr int VT_BYTES = NWAVES * D * VTS * 2;
+    static constexpr int MERGE_BYTES = (NWAVES * D * 16 + 2 * NWAVES * 16) * 4;
+    static constexpr int SMEM = VT_BYTES > MERGE_BYTES ? VT_BYTES : MERGE_BYTES;
+};
+
+template <int D>
+__global__ __launch_bounds__(NTHREADS) void decode_bf16_kernel(DecodeParams p) {
+    constexpr int NS = DecCfg<D>::NS, NDT = DecCfg<D>::NDT, NVB = DecCfg<D>::NVB;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[DecCfg<D>::SMEM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int qi = lane & 15, kq = lane >> 4;
+
+    // blockIdx.x -> (query slice, split, K/V head, batch); slices fastest.
+    int id = blockIdx.x;
+    const int qs = id % p.n_qs;
+    id /= p.n_qs;
+    const int split = id % p.num_splits;
+    id /= p.num_splits;
+    const int kvh = id % p.Hkv;
+    const int b = id / p.Hkv;
+
+    const int qg = qs * 16 + qi;  // head within the group
+    const bool q_ok = qg < p.G;
+    const int head = kvh * p.G + qg;
+
+    const int k_lo = min(p.Sk, split * p.split_chunk);
+    const int k_hi = min(p.Sk, k_lo + p.split_chunk);
+
+    // Q^T fragment (B operand): head_dim elements 32*s + 8*kq + j of query qi.
+    bf16x8 qf[NS];
+    {
+        const __bf16 *qrow = (const __bf16 *)p.q + ((int64_t)b * p.Hq + head) * D + 8 * kq;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            qf[s] = q_ok ? *(const bf16x8 *)(qrow + 32 * s)
+                         : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    }
+
+    const int64_t kv_stride = (int64_t)p.Hkv * D;
+    const __bf16 *kbase = (const __bf16 *)p.k + ((int64_t)b * p.Sk * p.Hkv + kvh) * D;
+    const __bf16 *vbase = (const __bf16 *)p.v + ((int64_t)b * p.Sk * p.Hkv + kvh) * D;
+    __bf16 *vt = (__bf16 *)smem + wave * D * VTS;
+
+    bf16x8 kf[2][NS];
+    u32x4 vreg[NVB][4];
+    bf16x8 kf_n[2][NS];
+    u32x4 vreg_n[NVB][4];
+
+    auto load = [&](int t0, bf16x8 (&kd)[2][NS], u32x4 (&vd)[NVB][4]) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const int key = t0 + 16 * kt + qi;
+            const __bf16 *krow = kbase + key * kv_stride + 8 * kq;
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                kd[kt][s] = key < k_hi ? *(const bf16x8 *)(krow + 32 * s)
+                                       : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        }
+#pragma unroll
+        for (int i = 0; i < NVB; ++i) {
+            const int blk = lane + 64 * i;
+            const int a = blk & 7, c = blk >> 3;
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int key = t0 + 4 * a + qq;
+                vd[i][qq] = key < k_hi ? *(const u32x4 *)(vbase + key * kv_stride + c * 8)
+                                       : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+
+    const float c = p.scale_log2;
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 oacc[NDT];
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) oacc[i] = f32x4{};
+
+    int t0 = k_lo + TK * wave;
+    if (t0 < k_hi) load(t0, kf, vreg);
+    for (; t0 < k_hi; t0 += TK * NWAVES) {
+        // V tile -> wave-private LDS, transposed to [d][key].
+#pragma unroll
+        for (int i = 0; i < NVB; ++i) {
+            const int blk = lane + 64 * i;
+            const int a = blk & 7, cc = blk >> 3;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                __bf16 *lo = vt + (cc * 8 + 2 * m) * VTS + 4 * a;
+                *(u32x2 *)lo = u32x2{pack_lo(vreg[i][0][m], vreg[i][1][m]),
+                                     pack_lo(vreg[i][2][m], vreg[i][3][m])};
+                *(u32x2 *)(lo + VTS) = u32x2{pack_hi(vreg[i][0][m], vreg[i][1][m]),
+                                             pack_hi(vreg[i][2][m], vreg[i][3][m])};
+            }
+        }
+        const int tn = t0 + TK * NWAVES;
+        if (tn < k_hi) load(tn, kf_n, vreg_n);
+
+        // S^T = K Q^T: 2 tiles of 16 keys x 16 query heads.
+        f32x4 sacc[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            sacc[kt] = f32x4{};
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][s], qf[s], sacc[kt], 0, 0, 0);
+        }
+        if (t0 + TK > k_hi) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (t0 + 16 * kt + 4 * kq + r >= k_hi) sacc[kt][r] = -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kt][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = pair_max32(mx);
+        const float m_new = fmaxf(m_run, mx * c);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < NDT; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oacc[i][r] *= alpha;
+        bf16x8 pf;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float pv = fast_exp2(fmaf(sacc[kt][r], c, -m_use));
+                l_run += pv;
+                pf[4 * kt + r] = (__bf16)pv;
+            }
+
+        // O^T += V^T P^T; k-slot j of lane (qi, kq) is key 16*(j/4) + 4*kq + j%4.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int i = 0; i < NDT; ++i) {
+            const __bf16 *vrow = vt + (16 * i + qi) * VTS + 4 * kq;
+            const u32x2 lo = *(const u32x2 *)vrow;
+            const u32x2 hi = *(const u32x2 *)(vrow + 16);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+            oacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, oacc[i], 0, 0, 0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        if (tn < k_hi) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int s = 0; s < NS; ++s) kf[kt][s] = kf_n[kt][s];
+#pragma unroll
+            for (int i = 0; i < NVB; ++i)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) vreg[i][qq] = vreg_n[i][qq];
+        }
+    }
+
+    // Sum this wave's l over the 4 lanes that share a query.
+    l_run += __shfl_xor(l_run, 16);
+    l_run = pair_sum32(l_run);
+
+    // Merge the 4 waves' (m, l, O^T) through LDS.
+    __syncthreads();
+    float *mo = (float *)smem;               // [wave][d][16]
+    float *mm = mo + NWAVES * D * 16;        // [wave][16]
+    float *ml = mm + NWAVES * 16;            // [wave][16]
+#pragma unroll
+    for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mo[(wave * D + 16 * i + 4 * kq + r) * 16 + qi] = oacc[i][r];
+    if (kq == 0) {
+        mm[wave * 16 + qi] = m_run;
+        ml[wave * 16 + qi] = l_run;
+    }
+    __syncthreads();
+
+    const int rows = p.B * p.Hq;
+    for (int idx = tid; idx < 16 * D; idx += NTHREADS) {
+        const int q2 = idx / D, d = idx - q2 * D;
+        const int g2 = qs * 16 + q2;
+        if (g2 >= p.G) continue;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NWAVES; ++w) M = fmaxf(M, mm[w * 16 + q2]);
+        float o = 0.f, l = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < NWAVES; ++w) {
+                const float f = fast_exp2(mm[w * 16 + q2] - M);
+                l += f * ml[w * 16 + q2];
+                o += f * mo[(w * D + d) * 16 + q2];
+            }
+        }
+        const bool empty = !(l > 0.f);
+        const float val = empty ? 0.f : o / l;
+        const float lse = empty ? -INFINITY : (M + log2f(l)) * kLn2;
+        const int64_t row = (int64_t)b * p.Hq + kvh * p.G + g2;
+        if (p.num_splits == 1) {
+            ((__bf16 *)p.o)[row * D + d] = (__bf16)val;
+            if (d == 0) p.lse[row] = lse;
+        } else {
+            const int64_t prow = (int64_t)split * rows + row;
+            p.ws_o[prow * D + d] = val;
+            if (d == 0) p.ws_lse[prow] = lse;
+        }
+    }
+}
+
+// Merge num_splits partials per (batch, head) row: one wavefront per row.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ ws_o,
+                                                      const float *__restrict__ ws_lse,
+                                                      void *out, float *lse, int rows, int ns) {
+    constexpr int PER = D / 64;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, ws_lse[(int64_t)s * rows + row]);
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+    float tot = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < ns; ++s) {
+            const float w = __expf(ws_lse[(int64_t)s * rows + row] - M);
+            tot += w;
+            const float *src = ws_o + ((int64_t)s * rows + row) * D;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, src[lane + 64 * e], acc[e]);
+        }
+    }
+    const bool empty = !(tot > 0.f);
+    const float inv = empty ? 0.f : 1.f / tot;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const float val = acc[e] * inv;
+        if (OUT_BF16)
+            ((__bf16 *)out)[(int64_t)row * D + lane + 64 * e] = (__bf16)val;
+        else
+            ((float *)out)[(int64_t)row * D + lane + 64 * e] = val;
+    }
+    if (lane == 0) lse[row] = empty ? -INFINITY : M + logf(tot);
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const DecodeParams &p, int d, hipStream_t s) {
+    const long long grid = (long long)p.B * p.Hkv * p.num_splits * p.n_qs;
+    if (d == 64) {
+        hipLaunchKernelGGL(decode_bf16_kernel<64>, dim3((unsigned)grid), dim3(NTHREADS), 0, s, p);
+    } else if (d == 128) {
+        hipLaunchKernelGGL(decode_bf16_kernel<128>, dim3((unsigned)grid), dim3(NTHREADS), 0, s, p);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_combine(const float *ws_o, const float *ws_lse, void *out, float *lse,
+                                 int rows, int num_splits, int d, bool out_bf16, hipStream_t s) {
+    const unsigned grid = (unsigned)((rows + 3) / 4);
+#define GQA_CASE(D_, B_)                                                                        \
+    if (d == D_ && out_bf16 == B_) {                                                            \
+        hipLaunchKernelGGL((combine_kernel<D_, B_>), dim3(grid), dim3(256), 0, s, ws_o, ws_lse, \
+                           out, lse, rows, num_splits);                                         \
+        return hipGetLastError();                                                               \
+    }
+    GQA_CASE(64, true)
+    GQA_CASE(64, false)
+    GQA_CASE(128, true)
+    GQA_CASE(128, false)
+#undef GQA_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gqa

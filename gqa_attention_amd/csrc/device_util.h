@@ -1,0 +1,44 @@
+// Small device helpers for gfx950 (CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Combine a value with the one held by lane (l ^ 32). v_permlane32_swap
+// exchanges the two 32-lane halves, so (r[0], r[1]) hold the pair
+// {x[l % 32], x[l % 32 + 32]} in every lane; a symmetric op on them is the
+// same, bit for bit, in both lanes of a pair.
+__device__ __forceinline__ float pair_max32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); exact 0 for -inf.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Pack the low / high bf16 halves of two dwords: (lo(a), lo(b)) and (hi(a), hi(b)).
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+    return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+    return (a >> 16) | (b & 0xffff0000u);
+}
+
+}  // namespace gqa

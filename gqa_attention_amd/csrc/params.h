@@ -1,0 +1,56 @@
+// Launch parameters shared by the host launchers and the kernels.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace gqa {
+
+// One forward launch (prefill / encoder). A "head group" is the set of query
+// heads one workgroup packs into its row tile: the G = Hq / Hkv heads that
+// share a K/V head (pack_gqa) or a single query head when packing is off.
+struct FwdParams {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    const int32_t *cu_q, *cu_k;  // both null for fixed length
+    int B, Hq, Hkv, Sq, Sk;      // Sq / Sk: lengths, or the maxima for variable length
+    int G;                       // Hq / Hkv
+    int gpack;                   // query heads per row tile: G or 1
+    int n_hg;                    // B * Hq / gpack
+    int n_rb;                    // row tiles per head group
+    float scale;                 // softmax scale (> 0)
+    float scale_log2;            // scale * log2(e)
+    // split-KV partial mode (fp32 kernel only, Sq == 1): key range of split s
+    // is [s * split_chunk, (s + 1) * split_chunk); partials go to ws_o / ws_lse.
+    int num_splits;
+    int split_chunk;
+    float *ws_o;
+    float *ws_lse;
+};
+
+// One split-KV decode launch (bf16 kernel).
+struct DecodeParams {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    int B, Hq, Hkv, Sk, G;
+    int n_qs;          // query slices of 16 heads per K/V head: ceil(G / 16)
+    int num_splits;
+    int split_chunk;   // keys per split (multiple of 64)
+    float scale_log2;
+    float *ws_o;       // [num_splits, B*Hq, d] fp32, used when num_splits > 1
+    float *ws_lse;     // [num_splits, B*Hq] fp32
+};
+
+// Launchers (one per kernel family). Each returns a hipError_t.
+hipError_t launch_fwd_bf16(const FwdParams &p, int d, bool causal, bool varlen, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdParams &p, int d, bool causal, bool varlen, bool split,
+                          hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeParams &p, int d, hipStream_t s);
+hipError_t launch_decode_combine(const float *ws_o, const float *ws_lse, void *out, float *lse,
+                                 int rows, int num_splits, int d, bool out_bf16, hipStream_t s);
+
+}  // namespace gqa

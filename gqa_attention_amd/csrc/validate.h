@@ -1,0 +1,85 @@
+// Host-side argument checks for the C ABI. Plain C++ with no HIP dependency:
+// every check runs before anything touches the GPU, so every error path can be
+// exercised on a machine without one.
+#pragma once
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "gqa_attn.h"
+
+namespace gqa {
+
+constexpr int kMaxSplits = 64;
+constexpr int kSplitAlign = 64;  // split chunk granularity (keys)
+
+inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline bool supported_d(int d) { return d == 64 || d == 128; }
+
+inline int check_common(int dtype, int d, float scale) {
+    if (dtype != GQA_DTYPE_BF16 && dtype != GQA_DTYPE_FP32) return GQA_EUNSUPPORTED;
+    if (!supported_d(d)) return GQA_EUNSUPPORTED;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return GQA_EINVAL;
+    return GQA_OK;
+}
+
+inline int validate_fwd(const void *q, const void *k, const void *v, const void *out,
+                        const float *lse, int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                        float scale, const int32_t *cu_q, const int32_t *cu_k, int dtype) {
+    if (!q || !k || !v || !out || !lse) return GQA_EINVAL;
+    const int rc = check_common(dtype, d, scale);
+    if (rc != GQA_OK) return rc;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return GQA_EINVAL;
+    const bool varlen = cu_q != nullptr;
+    if ((cu_q == nullptr) != (cu_k == nullptr)) return GQA_EINVAL;
+    if (varlen) {
+        if (Sq < 0 || Sk < 0) return GQA_EINVAL;
+        if (!aligned(cu_q, 4) || !aligned(cu_k, 4)) return GQA_EINVAL;
+    } else if (Sq < 1 || Sk < 1) {
+        return GQA_EINVAL;
+    }
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(lse, 4))
+        return GQA_EINVAL;
+    // Launch grid: head groups x row tiles must fit a 1-D grid (<= 2^31 - 1).
+    const long long tiles = ((long long)Hq * Sq + 31) / 32;
+    if ((long long)B * tiles > 0x7fffffffLL) return GQA_EINVAL;
+    return GQA_OK;
+}
+
+inline size_t decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
+    if (B < 1 || Hq < 1 || !supported_d(d) || num_splits < 1 || num_splits > kMaxSplits) return 0;
+    if (num_splits == 1) return 0;
+    const size_t rows = (size_t)B * Hq * num_splits;
+    size_t o_bytes = rows * d * sizeof(float);
+    o_bytes = (o_bytes + 255) & ~size_t(255);
+    return o_bytes + rows * sizeof(float);
+}
+
+inline int split_chunk(int Sk, int num_splits) {
+    int chunk = (Sk + num_splits - 1) / num_splits;
+    return (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+}
+
+inline int validate_decode(const void *q, const void *kc, const void *vc, const void *out,
+                           const float *lse, int B, int Hq, int Hkv, int Sk, int d, float scale,
+                           int num_splits, const void *ws, size_t ws_bytes, int dtype) {
+    if (!q || !kc || !vc || !out || !lse) return GQA_EINVAL;
+    const int rc = check_common(dtype, d, scale);
+    if (rc != GQA_OK) return rc;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sk < 1 || Hq % Hkv != 0) return GQA_EINVAL;
+    if (num_splits < 1 || num_splits > kMaxSplits) return GQA_EINVAL;
+    if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16) || !aligned(out, 16) ||
+        !aligned(lse, 4))
+        return GQA_EINVAL;
+    if ((long long)B * Hkv * num_splits * ((Hq / Hkv + 15) / 16) > 0x7fffffffLL) return GQA_EINVAL;
+    if (num_splits > 1) {
+        if (!ws || !aligned(ws, 16)) return GQA_EWORKSPACE;
+        if (ws_bytes < decode_workspace_bytes(B, Hq, d, num_splits)) return GQA_EWORKSPACE;
+    }
+    return GQA_OK;
+}
+
+}  // namespace gqa

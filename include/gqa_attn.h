@@ -1,0 +1,127 @@
+/*
+ * gqa_attn.h - C ABI of the MI355X (gfx950) fused grouped-query attention
+ * forward and split-KV decode.
+ *
+ * What is computed (per query head h, query row i):
+ *   O[i, h, :] = softmax_j(scale * q[i, h, :] . k[j, h / G, :]  (+ causal mask)) . v[j, h / G, :]
+ *   LSE[h, i]  = log sum_j exp(scale * q[i, h, :] . k[j, h / G, :])   (natural log)
+ * with G = Hq / Hkv query heads sharing each K/V head.
+ *
+ * Sources (the pages these kernels are built from):
+ *  - FlashAttention-2 summary (azimuth.plus): standard attention S = QK^T,
+ *    P = row softmax, O = PV; the tiled streaming softmax with a running max
+ *    and an unnormalised output rescaled by exp(m_old - m_new), one final
+ *    division by l, and the stored statistic L = m + log(l); work split over
+ *    batch x heads x query-row blocks; causal masking (diagonal kept) with
+ *    whole-tile skipping above the diagonal; GQA through index arithmetic
+ *    instead of copying K/V.
+ *  - Ultralytics glossary "Grouped Query Attention (GQA)", section "How GQA
+ *    works": query head h uses K/V head floor(h / G) (repeat_interleave).
+ *  - gitcode GQA batch-size guide, PackGQA paragraph and parameter table:
+ *    the query heads of one group packed into one thread block, the
+ *    query-head -> K/V-head map fixed ahead of the loop, and the split count
+ *    num_splits for the key range.
+ *  - Raptor-T abstract (icslab.whu.edu.cn): variable-length inputs without
+ *    padding; here packed sequences addressed by prefix offsets.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    allocates nothing, keeps no mutable global state, never synchronises and
+ *    never reads device data on the host.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream). Results are ready when the stream has reached the call.
+ *  - Tensors are dense and contiguous with head_dim innermost. q, k, v, out
+ *    and workspace must be 16-byte aligned; lse and cu_seqlens 4-byte aligned.
+ *  - Supported head_dim d: 64 and 128. dtype GQA_DTYPE_BF16 (bf16 in and out,
+ *    bf16 matrix-core products with fp32 accumulation) or GQA_DTYPE_FP32
+ *    (fp32 in and out, fp32 arithmetic throughout). lse is always fp32.
+ *  - `scale` must be finite and > 0 (the usual value is 1/sqrt(d)).
+ *  - A row that sees no key (causal with Lq > Lk, or an empty key range) gets
+ *    O = 0 and LSE = -inf.
+ *  - Every function returns a status; argument errors are reported before
+ *    anything is launched. Errors inside device data (e.g. a cu_seqlens array
+ *    that is not non-decreasing or exceeds the stated maxima) are not detected
+ *    and give undefined results.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GQA_DTYPE_BF16 = 0,
+    GQA_DTYPE_FP32 = 1
+} gqa_dtype;
+
+enum {
+    GQA_OK = 0,
+    GQA_EINVAL = 1,        /* bad argument: null pointer, bad size, head ratio, scale, alignment */
+    GQA_EUNSUPPORTED = 2,  /* head_dim not in {64, 128} or unknown dtype */
+    GQA_EWORKSPACE = 3,    /* decode workspace NULL or too small for num_splits > 1 */
+    GQA_ELAUNCH = 4        /* the HIP runtime refused a kernel launch */
+};
+
+/*
+ * gqa_attn_fwd - exact attention forward (prefill / encoder), fixed length or
+ * variable length.
+ *
+ * Fixed length (cu_seqlens_q == cu_seqlens_k == NULL):
+ *   q   [B, Sq, Hq,  d]   out [B, Sq, Hq, d] (same dtype as q)
+ *   k,v [B, Sk, Hkv, d]   lse [B, Hq, Sq] fp32
+ * Variable length (both cu_seqlens given, int32 [B+1] on the device,
+ * cu[0] = 0, non-decreasing; sequence b owns query rows cu_q[b]..cu_q[b+1]-1
+ * and keys cu_k[b]..cu_k[b+1]-1, no padding):
+ *   q   [total_q, Hq,  d]  out [total_q, Hq, d]
+ *   k,v [total_k, Hkv, d]  lse [total_q, Hq] fp32 (token-major)
+ *   Sq and Sk carry the largest per-sequence query / key length; they size
+ *   the launch grid only. A sequence longer than them is undefined.
+ * causal != 0 masks key j for query row i when j > i + (Lk - Lq) (per
+ * sequence; the diagonal is kept; bottom-right alignment when Lq != Lk).
+ * Requirements: B, Hq, Hkv >= 1; Sq, Sk >= 1 for fixed length and >= 0 for
+ * variable length; Hq % Hkv == 0.
+ */
+int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
+                 int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                 const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                 int dtype, void *stream);
+
+/*
+ * gqa_attn_decode_workspace_bytes - size of the caller-owned workspace that
+ * gqa_attn_decode needs for num_splits partial results (fp32 normalised
+ * partial outputs [num_splits, B*Hq, d] followed by fp32 partial LSEs
+ * [num_splits, B*Hq]). Returns 0 when num_splits == 1 (no workspace needed)
+ * and 0 for invalid sizes (num_splits < 1, B, Hq < 1, d not in {64, 128}).
+ */
+size_t gqa_attn_decode_workspace_bytes(int B, int Hq, int d, int num_splits);
+
+/*
+ * gqa_attn_decode - one new query token per sequence attending, without a
+ * mask, to its whole K/V cache, with the key range cut into num_splits
+ * contiguous ranges (gitcode GQA guide's num_splits) whose partial results are
+ * merged through their log-sum-exps:
+ *   L = M + log sum_s exp(L_s - M), M = max_s L_s;  O = sum_s exp(L_s - L) O_s.
+ *   q [B, Hq, d]; k_cache, v_cache [B, Sk, Hkv, d]; out [B, Hq, d]; lse [B, Hq].
+ * Split s covers keys [s*c, min(Sk, (s+1)*c)) with c = ceil(Sk/num_splits)
+ * rounded up to a multiple of 64; trailing splits may be empty and then
+ * contribute nothing. 1 <= num_splits <= 64. For num_splits > 1 the caller
+ * passes a device workspace of at least gqa_attn_decode_workspace_bytes().
+ * Results agree for every num_splits up to rounding.
+ */
+int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache, void *out,
+                    float *lse, int B, int Hq, int Hkv, int Sk, int d, float scale,
+                    int num_splits, void *workspace, size_t workspace_bytes,
+                    int dtype, void *stream);
+
+/* gqa_attn_strerror - static, NUL-terminated description of a status code. */
+const char *gqa_attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

@@ -1,0 +1,189 @@
+"""GPU parity: the HIP path against the fp64 oracle on seeded inputs.
+
+Shapes span several row tiles (128 packed rows for bf16, 32 for fp32) and key
+tiles (64 keys) with ragged tails, both head dims, MHA / GQA / MQA head
+ratios (including a group size that is not a power of two), causal and not,
+fixed and variable length, plus the degenerate cases: a single key, a single
+query, causal rows with no visible key, and empty sequences.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gqa_attention_amd as ga
+import gqa_inputs
+import oracle
+
+from parity_util import TOL, compare, oracle_fwd, run_fwd
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [torch.bfloat16, torch.float32]
+DT_ID = {torch.bfloat16: "bf16", torch.float32: "fp32"}
+
+FIXED = [
+    # B, Hq, Hkv, Sq, Sk, causal
+    (2, 8, 2, 200, 200, True),
+    (2, 8, 2, 200, 200, False),
+    (1, 4, 1, 130, 77, False),
+    (1, 4, 1, 77, 130, True),     # Lq < Lk: bottom-right causal
+    (1, 6, 2, 65, 300, False),    # G = 3
+    (1, 6, 2, 300, 65, True),     # Lq > Lk: early rows see no key
+    (2, 3, 3, 257, 129, False),   # MHA
+    (1, 2, 2, 1, 1, True),
+    (1, 8, 1, 1, 333, False),     # MQA, single query
+    (1, 16, 2, 33, 1, False),     # single key
+    (1, 32, 8, 512, 512, True),
+]
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DT_ID[d])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("shape", FIXED, ids=lambda s: "B{}_Hq{}_Hkv{}_Sq{}_Sk{}_{}".format(
+    *s[:5], "causal" if s[5] else "full"))
+def test_fixed(shape, d, dtype):
+    B, hq, hkv, sq, sk, causal = shape
+    w = gqa_inputs.fixed(B, hq, hkv, sq, sk, d, seed=1000 + sq * 7 + sk, dtype=dtype,
+                         causal=causal)
+    o, l = run_fwd(w)
+    ro, rl = oracle_fwd(w)
+    compare(o, l, ro, rl, dtype, f"fixed {shape} d={d}")
+
+
+VARLEN = [
+    # lengths_q, lengths_k, Hq, Hkv, causal
+    ([0, 1, 63, 64, 65, 200], [0, 1, 63, 64, 65, 200], 8, 2, True),
+    ([5, 130, 0, 17], [9, 100, 3, 17], 4, 4, False),
+    ([40, 130, 1], [20, 300, 7], 6, 2, True),
+    ([300], [300], 4, 1, True),
+]
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DT_ID[d])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: f"n{len(c[0])}_Hq{c[2]}_Hkv{c[3]}_{c[4]}")
+def test_varlen(case, d, dtype):
+    lq, lk, hq, hkv, causal = case
+    w = gqa_inputs.varlen(lq, lk, hq, hkv, d, seed=2000 + sum(lq), dtype=dtype, causal=causal)
+    o, l = run_fwd(w)
+    ro, rl = oracle_fwd(w)
+    compare(o, l, ro, rl, dtype, f"varlen {case} d={d}")
+
+
+DECODE = [
+    # B, Hq, Hkv, Sk
+    (3, 8, 2, 300),
+    (2, 32, 8, 1000),
+    (2, 32, 1, 129),   # MQA: 32 heads per K/V head (two 16-head slices)
+    (2, 12, 4, 77),    # G = 3
+    (1, 4, 4, 1),      # MHA, one cached key
+]
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DT_ID[d])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("ns", [1, 2, 4, 8])
+@pytest.mark.parametrize("shape", DECODE, ids=lambda s: "B{}_Hq{}_Hkv{}_Sk{}".format(*s))
+def test_decode(shape, ns, d, dtype):
+    B, hq, hkv, sk = shape
+    w = gqa_inputs.decode(B, hq, hkv, sk, d, seed=3000 + sk, dtype=dtype)
+    o, l = ga.decode(w.q.cuda(), w.k.cuda(), w.v.cuda(), scale=w.scale, num_splits=ns)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(w.q, w.k, w.v, w.scale)
+    compare(o.cpu(), l.cpu(), ro, rl, dtype, f"decode {shape} ns={ns} d={d}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DT_ID[d])
+def test_decode_partials_match_oracle_per_split(dtype):
+    """The workspace holds each split's normalised output and LSE."""
+    B, hq, hkv, sk, d, ns = 2, 8, 2, 300, 128, 4
+    w = gqa_inputs.decode(B, hq, hkv, sk, d, seed=77, dtype=dtype)
+    nbytes = ga.decode_workspace_bytes(B, hq, d, ns)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    ga.decode(w.q.cuda(), w.k.cuda(), w.v.cuda(), scale=w.scale, num_splits=ns, workspace=ws)
+    torch.cuda.synchronize()
+    rows = B * hq
+    o_bytes = ((ns * rows * d * 4 + 255) // 256) * 256
+    wso = ws[:ns * rows * d * 4].view(torch.float32).view(ns, B, hq, d).cpu()
+    wsl = ws[o_bytes:o_bytes + ns * rows * 4].view(torch.float32).view(ns, B, hq).cpu()
+    po, pl = oracle.decode_partials(w.q, w.k, w.v, w.scale, ns, align=64)
+    tol_o, tol_l = (2e-2, 1e-3) if dtype == torch.bfloat16 else (1e-5, 1e-5)
+    for s in range(ns):
+        compare(wso[s], wsl[s], po[s], pl[s], torch.float32 if dtype == torch.float32 else dtype,
+                f"split {s}")
+
+
+# ---------------------------------------------------------------------------
+# Invariants that hold bit for bit on the GPU.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_gqa_equals_expanded_mha_bitwise(causal):
+    """Glossary snippet: GQA equals MHA on repeat-interleaved K/V. Each row's
+    arithmetic is identical in both runs, so the results match bit for bit."""
+    w = gqa_inputs.fixed(2, 8, 2, 300, 300, 128, seed=5, causal=causal)
+    o1, l1 = run_fwd(w)
+    wx = gqa_inputs.Workload("mha", w.q, w.k.repeat_interleave(4, dim=2).contiguous(),
+                             w.v.repeat_interleave(4, dim=2).contiguous(), causal, w.scale)
+    o2, l2 = run_fwd(wx)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_varlen_equals_per_sequence_bitwise():
+    lens = [100, 1, 257, 64]
+    w = gqa_inputs.varlen(lens, lens, 8, 2, 128, seed=6, causal=True)
+    o, l = run_fwd(w)
+    cu = w.cu_seqlens_q.tolist()
+    for b in range(len(lens)):
+        wb = gqa_inputs.Workload("seq", w.q[None, cu[b]:cu[b + 1]].contiguous(),
+                                 w.k[None, cu[b]:cu[b + 1]].contiguous(),
+                                 w.v[None, cu[b]:cu[b + 1]].contiguous(), True, w.scale)
+        ob, lb = run_fwd(wb)
+        assert torch.equal(o[cu[b]:cu[b + 1]], ob[0])
+        assert torch.equal(l[cu[b]:cu[b + 1]], lb[0].T)
+
+
+@pytest.mark.parametrize("dtype", DTYPES, ids=lambda d: DT_ID[d])
+def test_causal_row0_is_v0(dtype):
+    """Row 0 of a causal Lq = Lk call sees only key 0: O = V[0] exactly."""
+    w = gqa_inputs.fixed(2, 8, 2, 100, 100, 128, seed=8, dtype=dtype, causal=True)
+    o, l = run_fwd(w)
+    for h in range(8):
+        assert torch.equal(o[:, 0, h], w.v[:, 0, h // 4])
+    q, k = w.q.double(), w.k.double()
+    want = torch.stack([(q[:, 0, h] * k[:, 0, h // 4]).sum(-1) for h in range(8)], 1) * float(
+        np.float32(w.scale))
+    assert torch.allclose(l[:, :, 0].double(), want, atol=TOL[dtype][1], rtol=0)
+
+
+def test_constant_v_gives_constant_output():
+    w = gqa_inputs.fixed(1, 8, 2, 150, 150, 64, seed=9, causal=True)
+    w.v = torch.full_like(w.v, 0.8125)  # exactly representable in bf16
+    o, _ = run_fwd(w)
+    assert torch.all(o == torch.tensor(0.8125, dtype=torch.bfloat16))
+
+
+def test_deterministic():
+    w = gqa_inputs.fixed(1, 32, 8, 700, 700, 128, seed=10, causal=True)
+    a = run_fwd(w)
+    b = run_fwd(w)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    d = gqa_inputs.decode(4, 32, 8, 999, 128, seed=11)
+    r1 = ga.decode(d.q.cuda(), d.k.cuda(), d.v.cuda(), num_splits=4)
+    r2 = ga.decode(d.q.cuda(), d.k.cuda(), d.v.cuda(), num_splits=4)
+    assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
+
+
+def test_num_splits_agree():
+    d = gqa_inputs.decode(4, 32, 8, 2000, 128, seed=12)
+    outs = [ga.decode(d.q.cuda(), d.k.cuda(), d.v.cuda(), num_splits=ns) for ns in (1, 2, 4, 8)]
+    for o, l in outs[1:]:
+        assert (o.float() - outs[0][0].float()).abs().max().item() <= 2e-2
+        assert (l - outs[0][1]).abs().max().item() <= 1e-3
+
+
+def test_empty_varlen_batch():
+    w = gqa_inputs.varlen([0, 0], [0, 5], 4, 2, 64, seed=13)
+    o, l = ga.fwd(w.q.cuda(), w.k.cuda(), w.v.cuda(), cu_seqlens_q=w.cu_seqlens_q.cuda(),
+                  cu_seqlens_k=w.cu_seqlens_k.cuda(), max_seqlen_q=0, max_seqlen_k=5)
+    assert o.numel() == 0 and l.numel() == 0

@@ -1,0 +1,152 @@
+"""Host-side checks of the C ABI that need no GPU.
+
+The library must load and export every function the header declares, and
+every argument error must be reported before anything is launched (so these
+calls never reach the device: the pointers below are fake but never
+dereferenced).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gqa_attention_amd as ga
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(ga.library_path()),
+                               reason="libgqa_attn.so not built")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced (validation fails first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(gqa_attn_\w+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_api():
+    assert declared_functions() == ["gqa_attn_decode", "gqa_attn_decode_workspace_bytes",
+                                    "gqa_attn_fwd", "gqa_attn_strerror"]
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    L = ga.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", ga.library_path()], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r" T (gqa_attn_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+@needs_lib
+def test_strerror():
+    assert ga.strerror(0) == "success"
+    for s in (1, 2, 3, 4):
+        assert ga.strerror(s) and ga.strerror(s) != "unknown status"
+    assert ga.strerror(99) == "unknown status"
+
+
+def fwd_call(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, B=1, Hq=8, Hkv=2, Sq=16, Sk=16, d=64,
+             scale=0.125, causal=1, cu_q=None, cu_k=None, dtype=0, stream=None)
+    a.update(kw)
+    return ga.lib().gqa_attn_fwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"],
+                                 a["Hkv"], a["Sq"], a["Sk"], a["d"], a["scale"], a["causal"],
+                                 a["cu_q"], a["cu_k"], a["dtype"], a["stream"])
+
+
+def dec_call(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, B=2, Hq=8, Hkv=2, Sk=100, d=128,
+             scale=0.1, ns=4, ws=FAKE, ws_bytes=1 << 30, dtype=0, stream=None)
+    a.update(kw)
+    return ga.lib().gqa_attn_decode(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"],
+                                    a["Hkv"], a["Sk"], a["d"], a["scale"], a["ns"], a["ws"],
+                                    a["ws_bytes"], a["dtype"], a["stream"])
+
+
+FWD_ERRORS = [
+    (dict(q=None), ga.GQA_EINVAL),
+    (dict(lse=None), ga.GQA_EINVAL),
+    (dict(d=96), ga.GQA_EUNSUPPORTED),
+    (dict(d=256), ga.GQA_EUNSUPPORTED),
+    (dict(dtype=7), ga.GQA_EUNSUPPORTED),
+    (dict(Hq=6, Hkv=4), ga.GQA_EINVAL),
+    (dict(Hkv=0), ga.GQA_EINVAL),
+    (dict(B=0), ga.GQA_EINVAL),
+    (dict(Sq=0), ga.GQA_EINVAL),
+    (dict(Sk=0), ga.GQA_EINVAL),
+    (dict(scale=float("nan")), ga.GQA_EINVAL),
+    (dict(scale=float("inf")), ga.GQA_EINVAL),
+    (dict(scale=0.0), ga.GQA_EINVAL),
+    (dict(scale=-0.5), ga.GQA_EINVAL),
+    (dict(cu_q=FAKE), ga.GQA_EINVAL),  # only one of the two offset arrays
+    (dict(cu_q=FAKE, cu_k=FAKE, Sq=-1), ga.GQA_EINVAL),
+    (dict(q=FAKE + 8), ga.GQA_EINVAL),  # misaligned
+    (dict(out=FAKE + 4), ga.GQA_EINVAL),
+    (dict(lse=FAKE + 2), ga.GQA_EINVAL),
+    (dict(cu_q=FAKE + 2, cu_k=FAKE), ga.GQA_EINVAL),
+]
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", FWD_ERRORS, ids=lambda x: str(x))
+def test_fwd_argument_errors(kw, code):
+    assert fwd_call(**kw) == code
+
+
+@needs_lib
+def test_fwd_varlen_without_rows_is_a_noop():
+    # variable length with max_seqlen_q == 0: nothing to compute, nothing launched
+    assert fwd_call(cu_q=FAKE, cu_k=FAKE, Sq=0, Sk=0) == ga.GQA_OK
+
+
+DEC_ERRORS = [
+    (dict(q=None), ga.GQA_EINVAL),
+    (dict(v=None), ga.GQA_EINVAL),
+    (dict(d=32), ga.GQA_EUNSUPPORTED),
+    (dict(dtype=-1), ga.GQA_EUNSUPPORTED),
+    (dict(Hq=9), ga.GQA_EINVAL),
+    (dict(Sk=0), ga.GQA_EINVAL),
+    (dict(ns=0), ga.GQA_EINVAL),
+    (dict(ns=65), ga.GQA_EINVAL),
+    (dict(scale=float("nan")), ga.GQA_EINVAL),
+    (dict(k=FAKE + 8), ga.GQA_EINVAL),
+    (dict(ws=None), ga.GQA_EWORKSPACE),
+    (dict(ws_bytes=1000), ga.GQA_EWORKSPACE),
+    (dict(ws=FAKE + 8), ga.GQA_EWORKSPACE),
+]
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", DEC_ERRORS, ids=lambda x: str(x))
+def test_decode_argument_errors(kw, code):
+    assert dec_call(**kw) == code
+
+
+@needs_lib
+def test_workspace_size():
+    f = ga.decode_workspace_bytes
+    assert f(64, 32, 128, 1) == 0
+    rows = 64 * 32 * 8
+    o = rows * 128 * 4
+    assert f(64, 32, 128, 8) == ((o + 255) // 256) * 256 + rows * 4
+    assert f(2, 8, 64, 2) >= 2 * 8 * 2 * 65 * 4
+    assert f(0, 8, 64, 2) == 0 and f(2, 8, 96, 2) == 0 and f(2, 8, 64, 0) == 0
+    assert f(2, 8, 64, 65) == 0
+    # exactly enough workspace is accepted by validation (fails only at launch, not run here)
+    need = f(2, 8, 128, 4)
+    assert dec_call(ws_bytes=need - 1) == ga.GQA_EWORKSPACE
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, RuntimeError)):
+        ga.fwd(q, q[:, :, :1].contiguous(), q[:, :, :1].contiguous())
