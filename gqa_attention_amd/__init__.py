@@ -13,6 +13,8 @@ Functions mirror the C entry points:
 * ``decode(q, k_cache, v_cache, scale=None, num_splits=1, workspace=None)`` ->
   ``(out, lse)``
 * ``decode_workspace_bytes(B, Hq, d, num_splits)``
+* ``FwdPlan`` / ``DecodePlan``: the same calls marshalled once, re-issued by
+  ``run()`` (for loops over fixed shapes and buffers)
 * ``strerror(status)``
 """
 from __future__ import annotations
@@ -24,7 +26,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["fwd", "decode", "decode_workspace_bytes", "strerror", "lib", "library_path",
+__all__ = ["fwd", "decode", "FwdPlan", "DecodePlan", "decode_workspace_bytes", "strerror", "lib", "library_path",
            "GQA_OK", "GQA_EINVAL", "GQA_EUNSUPPORTED", "GQA_EWORKSPACE", "GQA_ELAUNCH",
            "GQA_DTYPE_BF16", "GQA_DTYPE_FP32", "GqaError"]
 
@@ -112,19 +114,9 @@ def _stream_handle(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
-        scale: Optional[float] = None, cu_seqlens_q: Optional[torch.Tensor] = None,
-        cu_seqlens_k: Optional[torch.Tensor] = None, max_seqlen_q: Optional[int] = None,
-        max_seqlen_k: Optional[int] = None, out: Optional[torch.Tensor] = None,
-        lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Exact GQA attention forward through ``gqa_attn_fwd``.
-
-    Fixed length: q [B, Sq, Hq, d], k/v [B, Sk, Hkv, d] -> out like q,
-    lse fp32 [B, Hq, Sq]. Variable length: q [Tq, Hq, d], k/v [Tk, Hkv, d],
-    int32 cu_seqlens [B+1] on the device and the maximum lengths (which size
-    the grid; no host read of device data happens) -> lse fp32 [Tq, Hq].
-    ``scale`` defaults to 1/sqrt(d).
-    """
+def _prepare_fwd(q, k, v, causal, scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                 max_seqlen_k, out, lse):
+    """Check tensor metadata, allocate outputs, build the C argument tuple."""
     dt = q.dtype
     varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
     nd = 3 if varlen else 4
@@ -170,31 +162,64 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
         if tuple(lse.shape) != lse_shape:
             raise ValueError(f"lse must have shape {lse_shape}")
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    if q.numel() == 0:
-        return out, lse
-    with torch.cuda.device(dev):
-        st = lib().gqa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                lse.data_ptr(), B, Hq, Hkv, Sq, Sk, d, sc, int(bool(causal)),
-                                cq, ck, code, _stream_handle(dev))
-    _raise(st, "gqa_attn_fwd")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq,
+            Hkv, Sq, Sk, d, sc, int(bool(causal)), cq, ck, code)
+    return out, lse, args, q.numel() == 0
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+        scale: Optional[float] = None, cu_seqlens_q: Optional[torch.Tensor] = None,
+        cu_seqlens_k: Optional[torch.Tensor] = None, max_seqlen_q: Optional[int] = None,
+        max_seqlen_k: Optional[int] = None, out: Optional[torch.Tensor] = None,
+        lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Exact GQA attention forward through ``gqa_attn_fwd``.
+
+    Fixed length: q [B, Sq, Hq, d], k/v [B, Sk, Hkv, d] -> out like q,
+    lse fp32 [B, Hq, Sq]. Variable length: q [Tq, Hq, d], k/v [Tk, Hkv, d],
+    int32 cu_seqlens [B+1] on the device and the maximum lengths (which size
+    the grid; no host read of device data happens) -> lse fp32 [Tq, Hq].
+    ``scale`` defaults to 1/sqrt(d).
+    """
+    out, lse, args, empty = _prepare_fwd(q, k, v, causal, scale, cu_seqlens_q, cu_seqlens_k,
+                                         max_seqlen_q, max_seqlen_k, out, lse)
+    if not empty:
+        with torch.cuda.device(q.device):
+            st = lib().gqa_attn_fwd(*args, _stream_handle(q.device))
+        _raise(st, "gqa_attn_fwd")
     return out, lse
+
+
+class FwdPlan:
+    """A forward call with its arguments checked and marshalled once.
+
+    ``run()`` re-issues the same ``gqa_attn_fwd`` call on the current stream
+    (the tensors given at construction must stay alive and keep their
+    addresses); meant for loops that call the same shapes repeatedly.
+    """
+
+    def __init__(self, q, k, v, *, causal=False, scale=None, cu_seqlens_q=None,
+                 cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, out=None, lse=None):
+        self.out, self.lse, self._args, self._empty = _prepare_fwd(
+            q, k, v, causal, scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+            out, lse)
+        self._keep = (q, k, v, cu_seqlens_q, cu_seqlens_k)
+        self._dev = q.device
+        self._fn = lib().gqa_attn_fwd
+
+    def run(self):
+        if not self._empty:
+            st = self._fn(*self._args, _stream_handle(self._dev))
+            if st:
+                _raise(st, "gqa_attn_fwd")
+        return self.out, self.lse
 
 
 def decode_workspace_bytes(B: int, Hq: int, d: int, num_splits: int) -> int:
     return int(lib().gqa_attn_decode_workspace_bytes(B, Hq, d, num_splits))
 
 
-def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *,
-           scale: Optional[float] = None, num_splits: int = 1,
-           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-           lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Split-KV decode through ``gqa_attn_decode``.
-
-    q [B, Hq, d]; caches [B, Sk, Hkv, d] -> out [B, Hq, d], lse fp32 [B, Hq].
-    For num_splits > 1 a uint8 device workspace of
-    ``decode_workspace_bytes(B, Hq, d, num_splits)`` bytes is allocated unless
-    one is passed.
-    """
+def _prepare_decode(q, k_cache, v_cache, scale, num_splits, workspace, out, lse):
+    """Check tensor metadata, allocate outputs / workspace, build the C arguments."""
     dt = q.dtype
     dev = q.device
     _check("q", q, 3, dt, None)
@@ -217,9 +242,43 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *,
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    with torch.cuda.device(dev):
-        st = lib().gqa_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                   out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Sk, d, sc,
-                                   int(num_splits), ws_ptr, ws_bytes, code, _stream_handle(dev))
+    args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+            lse.data_ptr(), B, Hq, Hkv, Sk, d, sc, int(num_splits), ws_ptr, ws_bytes, code)
+    return out, lse, workspace, args
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *,
+           scale: Optional[float] = None, num_splits: int = 1,
+           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-KV decode through ``gqa_attn_decode``.
+
+    q [B, Hq, d]; caches [B, Sk, Hkv, d] -> out [B, Hq, d], lse fp32 [B, Hq].
+    For num_splits > 1 a uint8 device workspace of
+    ``decode_workspace_bytes(B, Hq, d, num_splits)`` bytes is allocated unless
+    one is passed.
+    """
+    out, lse, _, args = _prepare_decode(q, k_cache, v_cache, scale, num_splits, workspace,
+                                        out, lse)
+    with torch.cuda.device(q.device):
+        st = lib().gqa_attn_decode(*args, _stream_handle(q.device))
     _raise(st, "gqa_attn_decode")
     return out, lse
+
+
+class DecodePlan:
+    """A decode call checked and marshalled once; ``run()`` re-issues it."""
+
+    def __init__(self, q, k_cache, v_cache, *, scale=None, num_splits=1, workspace=None,
+                 out=None, lse=None):
+        self.out, self.lse, self.workspace, self._args = _prepare_decode(
+            q, k_cache, v_cache, scale, num_splits, workspace, out, lse)
+        self._keep = (q, k_cache, v_cache)
+        self._dev = q.device
+        self._fn = lib().gqa_attn_decode
+
+    def run(self):
+        st = self._fn(*self._args, _stream_handle(self._dev))
+        if st:
+            _raise(st, "gqa_attn_decode")
+        return self.out, self.lse

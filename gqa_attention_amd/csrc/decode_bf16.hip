@@ -18,8 +18,9 @@
 //    merged through LDS at the end.
 //  * v_mfma_f32_16x16x32_bf16 for S^T = K Q^T (16 keys x 16 query heads) with
 //    K loaded from HBM straight into the A-operand layout, and for
-//    O^T = V^T P^T with V transposed through a wave-private LDS buffer. The
-//    next tile's loads are issued before the current tile's math.
+//    O^T = V^T P^T with V staged row-major in a wave-private LDS slice and
+//    read as V^T with ds_read_b64_tr_b16. The next tile's loads are issued
+//    before the current tile's math.
 
 #include "device_util.h"
 #include "params.h"
@@ -31,21 +32,26 @@ namespace {
 constexpr int NTHREADS = 256;
 constexpr int NWAVES = 4;
 constexpr int TK = 32;        // keys per wave tile
-constexpr int VTS = TK + 4;   // LDS row stride of the wave's V^T tile (elements)
 
 template <int D>
 struct DecCfg {
     static constexpr int NS = D / 32;    // k-steps of 32 head_dim elements
     static constexpr int NDT = D / 16;   // 16-row tiles of O^T
-    static constexpr int NVB = D / 64;   // 4-key x 8-d V blocks per lane
-    static constexpr int VT_BYTES = NWAVES * D * VTS * 2;
+    static constexpr int NVL = D / 16;   // 16-byte V chunks per lane per tile
+    // V row stride in LDS (elements): the 32 lanes of a transposing read touch
+    // rows r..r+3 and r+4..r+7; a stride of D + 16 puts their 8 segments of
+    // 32 bytes on disjoint banks.
+    static constexpr int VRS = D + 16;
+    static constexpr int VT_BYTES = NWAVES * TK * VRS * 2;
     static constexpr int MERGE_BYTES = (NWAVES * D * 16 + 2 * NWAVES * 16) * 4;
     static constexpr int SMEM = VT_BYTES > MERGE_BYTES ? VT_BYTES : MERGE_BYTES;
 };
 
 template <int D>
 __global__ __launch_bounds__(NTHREADS) void decode_bf16_kernel(DecodeParams p) {
-    constexpr int NS = DecCfg<D>::NS, NDT = DecCfg<D>::NDT, NVB = DecCfg<D>::NVB;
+    constexpr int NS = DecCfg<D>::NS, NDT = DecCfg<D>::NDT, NVL = DecCfg<D>::NVL;
+    constexpr int VRS = DecCfg<D>::VRS;
+    constexpr int C8 = D / 8;
     __shared__ __attribute__((aligned(16))) unsigned char smem[DecCfg<D>::SMEM];
 
     const int tid = threadIdx.x;
@@ -81,35 +87,32 @@ __global__ __launch_bounds__(NTHREADS) void decode_bf16_kernel(DecodeParams p) {
     const int64_t kv_stride = (int64_t)p.Hkv * D;
     const __bf16 *kbase = (const __bf16 *)p.k + ((int64_t)b * p.Sk * p.Hkv + kvh) * D;
     const __bf16 *vbase = (const __bf16 *)p.v + ((int64_t)b * p.Sk * p.Hkv + kvh) * D;
-    __bf16 *vt = (__bf16 *)smem + wave * D * VTS;
+    __bf16 *vsw = (__bf16 *)smem + wave * TK * VRS;  // this wave's V tile, row-major
 
     bf16x8 kf[2][NS];
-    u32x4 vreg[NVB][4];
+    u32x4 vreg[NVL];
     bf16x8 kf_n[2][NS];
-    u32x4 vreg_n[NVB][4];
+    u32x4 vreg_n[NVL];
 
-    auto load = [&](int t0, bf16x8 (&kd)[2][NS], u32x4 (&vd)[NVB][4]) {
+    auto load = [&](int t0, bf16x8 (&kd)[2][NS], u32x4 (&vd)[NVL]) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-            const int key = t0 + 16 * kt + qi;
+            const int key = min(t0 + 16 * kt + qi, k_hi - 1);  // clamped; masked below
             const __bf16 *krow = kbase + key * kv_stride + 8 * kq;
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
-                kd[kt][s] = key < k_hi ? *(const bf16x8 *)(krow + 32 * s)
-                                       : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+            for (int s = 0; s < NS; ++s) kd[kt][s] = *(const bf16x8 *)(krow + 32 * s);
         }
 #pragma unroll
-        for (int i = 0; i < NVB; ++i) {
-            const int blk = lane + 64 * i;
-            const int a = blk & 7, c = blk >> 3;
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int key = t0 + 4 * a + qq;
-                vd[i][qq] = key < k_hi ? *(const u32x4 *)(vbase + key * kv_stride + c * 8)
-                                       : u32x4{0u, 0u, 0u, 0u};
-            }
+        for (int i = 0; i < NVL; ++i) {  // whole rows: 16-byte chunk lane + 64 i
+            const int c = lane + 64 * i;
+            const int key = min(t0 + c / C8, k_hi - 1);
+            vd[i] = *(const u32x4 *)(vbase + key * kv_stride + (c % C8) * 8);
         }
     };
+    // PV operand: in 16-lane group kq, lane j reads row 4 kq + j/4 (+16 for
+    // the second read), columns 16 dt + 4 (j%4) .. +3; ds_read_b64_tr_b16
+    // then gives lane j the column 16 dt + j of those 4 rows.
+    const int v_rd = (4 * kq + (qi >> 2)) * VRS + 4 * (qi & 3);
 
     const float c = p.scale_log2;
     float m_run = -INFINITY, l_run = 0.f;
@@ -120,19 +123,11 @@ __global__ __launch_bounds__(NTHREADS) void decode_bf16_kernel(DecodeParams p) {
     int t0 = k_lo + TK * wave;
     if (t0 < k_hi) load(t0, kf, vreg);
     for (; t0 < k_hi; t0 += TK * NWAVES) {
-        // V tile -> wave-private LDS, transposed to [d][key].
+        // V tile -> this wave's LDS slice, row-major.
 #pragma unroll
-        for (int i = 0; i < NVB; ++i) {
-            const int blk = lane + 64 * i;
-            const int a = blk & 7, cc = blk >> 3;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                __bf16 *lo = vt + (cc * 8 + 2 * m) * VTS + 4 * a;
-                *(u32x2 *)lo = u32x2{pack_lo(vreg[i][0][m], vreg[i][1][m]),
-                                     pack_lo(vreg[i][2][m], vreg[i][3][m])};
-                *(u32x2 *)(lo + VTS) = u32x2{pack_hi(vreg[i][0][m], vreg[i][1][m]),
-                                             pack_hi(vreg[i][2][m], vreg[i][3][m])};
-            }
+        for (int i = 0; i < NVL; ++i) {
+            const int c = lane + 64 * i;
+            *(u32x4 *)(vsw + (c / C8) * VRS + (c % C8) * 8) = vreg[i];
         }
         const int tn = t0 + TK * NWAVES;
         if (tn < k_hi) load(tn, kf_n, vreg_n);
@@ -160,15 +155,19 @@ __global__ __launch_bounds__(NTHREADS) void decode_bf16_kernel(DecodeParams p) {
             for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kt][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = pair_max32(mx);
-        const float m_new = fmaxf(m_run, mx * c);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        m_run = m_new;
-        l_run *= alpha;
+        // Move the reference max only when it is exceeded by more than
+        // kRescaleGap (see fwd_bf16.hip); the result is unchanged.
+        const float mxs = mx * c;
+        if (mxs > m_run + kRescaleGap) {
+            const float alpha = fast_exp2(m_run - mxs);
+            m_run = mxs;
+            l_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < NDT; ++i)
+            for (int i = 0; i < NDT; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) oacc[i][r] *= alpha;
+                for (int r = 0; r < 4; ++r) oacc[i][r] *= alpha;
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
         bf16x8 pf;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -185,9 +184,9 @@ __global__ __launch_bounds__(NTHREADS) void decode_bf16_kernel(DecodeParams p) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
         for (int i = 0; i < NDT; ++i) {
-            const __bf16 *vrow = vt + (16 * i + qi) * VTS + 4 * kq;
-            const u32x2 lo = *(const u32x2 *)vrow;
-            const u32x2 hi = *(const u32x2 *)(vrow + 16);
+            const __bf16 *vp = vsw + 16 * i + v_rd;
+            const u32x2 lo = lds_read_tr16(vp);
+            const u32x2 hi = lds_read_tr16(vp + 16 * VRS);
             const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
             oacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, oacc[i], 0, 0, 0);
         }
@@ -201,9 +200,7 @@ __global__ __launch_bounds__(NTHREADS) void decode_bf16_kernel(DecodeParams p) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) kf[kt][s] = kf_n[kt][s];
 #pragma unroll
-            for (int i = 0; i < NVB; ++i)
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) vreg[i][qq] = vreg_n[i][qq];
+            for (int i = 0; i < NVL; ++i) vreg[i] = vreg_n[i];
         }
     }
 

@@ -16,6 +16,10 @@ typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Largest amount (log2 units) by which a tile's row max may exceed the running
+// reference max before the unnormalised output is rescaled (p <= 2^8 = 256).
+constexpr float kRescaleGap = 8.0f;
+
 // Combine a value with the one held by lane (l ^ 32). v_permlane32_swap
 // exchanges the two 32-lane halves, so (r[0], r[1]) hold the pair
 // {x[l % 32], x[l % 32 + 32]} in every lane; a symmetric op on them is the
@@ -28,6 +32,19 @@ __device__ __forceinline__ float pair_max32(float x) {
 __device__ __forceinline__ float pair_sum32(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane j supplies the address of 4 consecutive 16-bit elements; viewing the
+// group's 64 elements as E[4j + e], lane c receives E[c], E[c+16], E[c+32],
+// E[c+48]. With lane j pointing at row (j / 4), columns 4 (j % 4) .. +3 of a
+// row-major tile, lane c gets the 4 rows of column c: a column slice of V as
+// the matrix-core operand of V^T.
+typedef short s16x4_lds __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const __bf16 *p) {
+    const s16x4_lds t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_lds *)(p));
+    return __builtin_bit_cast(u32x2, t);
 }
 
 // 2^x on the transcendental unit (v_exp_f32); exact 0 for -inf.

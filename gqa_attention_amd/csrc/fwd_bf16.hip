@@ -24,14 +24,16 @@
 //  * O^T = V^T P^T accumulates with the same lane <-> query ownership, so the
 //    rescale by exp(m_old - m_new) is a per-lane scalar multiply and P never
 //    leaves registers (its bf16 copy is the B operand as produced).
-//  * K is staged row-major in LDS; V is transposed on its way into LDS.
-//    Both are double-buffered, with the next tile's global loads in flight
-//    during the current tile's math (one barrier per tile).
+//  * K and V are staged row-major in LDS (coalesced 16-byte loads of whole
+//    rows); the V^T operand is read with ds_read_b64_tr_b16, which hands each
+//    lane a column slice. Double-buffered, with the next tile's global loads
+//    in flight during the current tile's math (one barrier per tile).
 //  * exp is 2^x on the transcendental unit with scale*log2(e) folded into one
 //    FMA; P and O are rounded to bf16 with round-to-nearest-even.
-//  * Workgroup order: head group fastest, so with 8 XCDs and a head-group
-//    count divisible by 8 each head group's K/V stays in one XCD's L2; causal
-//    row tiles are issued heaviest first.
+//  * Workgroup order: the row tiles of a head group run back to back on one
+//    XCD (workgroups are dealt round-robin to the 8 XCDs), so its K/V comes
+//    from HBM once and is then reused from that XCD's L2; causal row tiles are
+//    issued heaviest first.
 
 #include "device_util.h"
 #include "params.h"
@@ -46,31 +48,41 @@ constexpr int NTHREADS = 256;
 
 template <int D>
 struct Cfg {
-    static constexpr int KS = D + 8;            // LDS row stride of K (elements)
-    static constexpr int VS = BN + 4;           // LDS row stride of V^T (elements)
-    static constexpr int KQ = D == 128 ? 4 : 2; // keys per thread in the V transpose
-    static constexpr int NKL = BN * D / 8 / NTHREADS;  // 16-byte K chunks per thread
+    static constexpr int KS = D + 8;    // LDS row stride of K (elements): conflict-free b128 reads
+    static constexpr int VS = D + 32;   // LDS row stride of V (elements): conflict-free tr16 reads
+    static constexpr int NKL = BN * D / 8 / NTHREADS;  // 16-byte chunks per thread per tensor
 };
 
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdParams p) {
-    constexpr int KS = Cfg<D>::KS, VS = Cfg<D>::VS, KQ = Cfg<D>::KQ, NKL = Cfg<D>::NKL;
+    constexpr int KS = Cfg<D>::KS, VS = Cfg<D>::VS, NKL = Cfg<D>::NKL;
     constexpr int DSTEPS = D / 16;  // k-steps of the score product
     constexpr int DBLK = D / 32;    // 32-row blocks of O^T
     constexpr int KB = BN / 32;     // 32-key blocks per tile
     constexpr int C8 = D / 8;       // 16-byte chunks per K/V row
 
     __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * KS];
-    __shared__ __attribute__((aligned(16))) __bf16 Vt[2][D * VS];
+    __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BN * VS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int col = lane & 31, half = lane >> 5;
 
     // ---- workgroup -> (head group, row tile) ----
+    // Workgroups are dealt round-robin to the 8 XCDs (pid % 8). When the head
+    // groups split evenly over the XCDs, all row tiles of one head group run
+    // back to back on one XCD, so its K/V is fetched from HBM once and then
+    // served from that XCD's L2. Causal row tiles go heaviest first.
     const int pid = blockIdx.x;
-    const int hg = pid % p.n_hg;
-    const int rank = pid / p.n_hg;
+    int hg, rank;
+    if ((p.n_hg & 7) == 0) {
+        const int slot = pid >> 3;
+        hg = (slot / p.n_rb) * 8 + (pid & 7);
+        rank = slot % p.n_rb;
+    } else {
+        hg = pid / p.n_rb;
+        rank = pid % p.n_rb;
+    }
     const int rb = CAUSAL ? (p.n_rb - 1 - rank) : rank;
     const int hpb = p.Hq / p.gpack;
     const int b = hg / hpb;
@@ -137,49 +149,44 @@ __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2))) v
     const __bf16 *kbase = (const __bf16 *)p.k + ((int64_t)k_tok0 * p.Hkv + kvh) * D;
     const __bf16 *vbase = (const __bf16 *)p.v + ((int64_t)k_tok0 * p.Hkv + kvh) * D;
 
-    // V transpose ownership: keys [va*KQ, va*KQ + KQ) x d [vc*8, vc*8 + 8)
-    const int va = tid % (BN / KQ);
-    const int vc = tid / (BN / KQ);
+    // Tile staging: thread tid moves 16-byte chunks tid + 256 i (row-major,
+    // D/8 chunks per row) of K and of V. Offsets are fixed per thread.
+    int g_off[NKL], k_soff[NKL], v_soff[NKL], row_of[NKL];
+#pragma unroll
+    for (int i = 0; i < NKL; ++i) {
+        const int c = tid + NTHREADS * i;
+        row_of[i] = c / C8;
+        g_off[i] = (c % C8) * 8;
+        k_soff[i] = row_of[i] * KS + g_off[i];
+        v_soff[i] = row_of[i] * VS + g_off[i];
+    }
+    u32x4 kreg[NKL], vreg[NKL];
 
-    u32x4 kreg[NKL];
-    u32x4 vreg[KQ];
-
+    // Rows past kend are clamped to the last needed key: they are real, finite
+    // K/V rows, their scores are masked to -inf and their p is exactly 0.
     auto load_tile = [&](int t) {
 #pragma unroll
         for (int i = 0; i < NKL; ++i) {
-            const int c = tid + NTHREADS * i;
-            const int r = c / C8, c8 = c % C8;
-            const int key = t * BN + r;
-            kreg[i] = key < kend ? *(const u32x4 *)(kbase + key * kv_stride + c8 * 8)
-                                 : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int qq = 0; qq < KQ; ++qq) {
-            const int key = t * BN + va * KQ + qq;
-            vreg[qq] = key < kend ? *(const u32x4 *)(vbase + key * kv_stride + vc * 8)
-                                  : u32x4{0u, 0u, 0u, 0u};
+            const int64_t off = (int64_t)min(t * BN + row_of[i], kend - 1) * kv_stride + g_off[i];
+            kreg[i] = *(const u32x4 *)(kbase + off);
+            vreg[i] = *(const u32x4 *)(vbase + off);
         }
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < NKL; ++i) {
-            const int c = tid + NTHREADS * i;
-            const int r = c / C8, c8 = c % C8;
-            *(u32x4 *)(&Ks[buf][r * KS + c8 * 8]) = kreg[i];
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            __bf16 *lo = &Vt[buf][(vc * 8 + 2 * m) * VS + va * KQ];
-            __bf16 *hi = lo + VS;
-            if constexpr (KQ == 4) {
-                *(u32x2 *)lo = u32x2{pack_lo(vreg[0][m], vreg[1][m]), pack_lo(vreg[2][m], vreg[3][m])};
-                *(u32x2 *)hi = u32x2{pack_hi(vreg[0][m], vreg[1][m]), pack_hi(vreg[2][m], vreg[3][m])};
-            } else {
-                *(uint32_t *)lo = pack_lo(vreg[0][m], vreg[1][m]);
-                *(uint32_t *)hi = pack_hi(vreg[0][m], vreg[1][m]);
-            }
+            *(u32x4 *)(&Ks[buf][k_soff[i]]) = kreg[i];
+            *(u32x4 *)(&Vs[buf][v_soff[i]]) = vreg[i];
         }
     };
+
+    // V^T operand through ds_read_b64_tr_b16: in 16-lane group g, lane j reads
+    // row key0 + j/4, columns d0 + 4 (j%4) .. +3 and receives column d0 + j of
+    // rows key0 .. key0+3, with d0 = 32 i + 16 (g & 1) and key0 = 4 (g >> 1)
+    // (+ 8 for the second read) inside the 16-key slot.
+    const int vj = lane & 15, vg = lane >> 4;
+    const int v_rd = (4 * (vg >> 1) + (vj >> 2)) * VS + 16 * (vg & 1) + 4 * (vj & 3);
+    const int k_rd = col * KS + 8 * half;
 
     const float c = p.scale_log2;
     float m_run = -INFINITY;  // running max of scaled scores, log2 units
@@ -201,14 +208,14 @@ __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2))) v
 
         if (wave_live && t * BN < wave_kend) {
             const __bf16 *ks = Ks[cur];
-            const __bf16 *vt = Vt[cur];
+            const __bf16 *vs = Vs[cur];
 
             // S^T tile: rows = keys, columns = this wave's 32 query rows.
             f32x16 sacc[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 sacc[kb] = f32x16{};
-                const __bf16 *krow = ks + (kb * 32 + col) * KS + 8 * half;
+                const __bf16 *krow = ks + kb * 32 * KS + k_rd;
 #pragma unroll
                 for (int s = 0; s < DSTEPS; ++s) {
                     const bf16x8 a = *(const bf16x8 *)(krow + 16 * s);
@@ -234,15 +241,21 @@ __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
             mx = pair_max32(mx);
-            const float m_new = fmaxf(m_run, mx * c);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_use);
-            m_run = m_new;
-            l_run *= alpha;
+            // The reference max only moves when the tile max exceeds it by more
+            // than kRescaleGap (log2 units); every p then stays <= 2^kRescaleGap
+            // and the rescale of O~ is skipped on almost every tile. The result
+            // is the same: m cancels between O~ and l and is added back in L.
+            const float mxs = mx * c;
+            if (mxs > m_run + kRescaleGap) {
+                const float alpha = fast_exp2(m_run - mxs);
+                m_run = mxs;
+                l_run *= alpha;
 #pragma unroll
-            for (int i = 0; i < DBLK; ++i)
+                for (int i = 0; i < DBLK; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+                    for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+            }
+            const float m_use = m_run == -INFINITY ? 0.f : m_run;
 
             bf16x8 pf[KB][2];
 #pragma unroll
@@ -264,9 +277,9 @@ __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2))) v
                 for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                     for (int i = 0; i < DBLK; ++i) {
-                        const __bf16 *vrow = vt + (i * 32 + col) * VS + kb * 32 + 16 * h2 + 4 * half;
-                        const u32x2 lo = *(const u32x2 *)vrow;
-                        const u32x2 hi = *(const u32x2 *)(vrow + 8);
+                        const __bf16 *vp = vs + (kb * 32 + 16 * h2) * VS + 32 * i + v_rd;
+                        const u32x2 lo = lds_read_tr16(vp);
+                        const u32x2 hi = lds_read_tr16(vp + 8 * VS);
                         const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
                         oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][h2], oacc[i], 0, 0, 0);
                     }
