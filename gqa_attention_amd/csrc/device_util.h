@@ -47,6 +47,25 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const __bf16 *p) {
     return __builtin_bit_cast(u32x2, t);
 }
 
+// Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes land at LDS byte address lds_base + 16 l, lds_base being
+// wave-uniform (M0). Written as asm so that the compiler does not track it:
+// callers wait for completion themselves with s_waitcnt vmcnt. It has no
+// register outputs; its inputs are read when it issues. The compiler's own
+// vmcnt waits do not count these loads and can therefore only over-wait.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved; nothing else here uses it
+__device__ __forceinline__ void lds_dma16(const void *gptr, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_base), "v"(gptr)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
 // 2^x on the transcendental unit (v_exp_f32); exact 0 for -inf.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -24,16 +24,21 @@
 //  * O^T = V^T P^T accumulates with the same lane <-> query ownership, so the
 //    rescale by exp(m_old - m_new) is a per-lane scalar multiply and P never
 //    leaves registers (its bf16 copy is the B operand as produced).
-//  * K and V are staged row-major in LDS (coalesced 16-byte loads of whole
-//    rows); the V^T operand is read with ds_read_b64_tr_b16, which hands each
-//    lane a column slice. Double-buffered, with the next tile's global loads
-//    in flight during the current tile's math (one barrier per tile).
+//  * K and V are staged row-major in LDS by direct global->LDS loads of whole
+//    rows (no staging registers); the V^T operand is read with
+//    ds_read_b64_tr_b16, which hands each lane a column slice.
+//    Double-buffered and software-pipelined: the scores
+//    of tile t+1 run on the matrix cores while the vector units exponentiate
+//    tile t, with the global loads of the following tiles in flight (one
+//    barrier per tile).
 //  * exp is 2^x on the transcendental unit with scale*log2(e) folded into one
 //    FMA; P and O are rounded to bf16 with round-to-nearest-even.
 //  * Workgroup order: the row tiles of a head group run back to back on one
 //    XCD (workgroups are dealt round-robin to the 8 XCDs), so its K/V comes
 //    from HBM once and is then reused from that XCD's L2; causal row tiles are
 //    issued heaviest first.
+
+#include <type_traits>
 
 #include "device_util.h"
 #include "params.h"
@@ -42,27 +47,73 @@ namespace gqa {
 
 namespace {
 
-constexpr int BM = 128;  // packed query rows per workgroup
-constexpr int BN = 64;   // keys per tile
-constexpr int NTHREADS = 256;
+#ifndef GQA_BN128
+#define GQA_BN128 32
+#endif
+#ifndef GQA_PF_K
+#define GQA_PF_K 6
+#endif
+#ifndef GQA_VR_DIV
+#define GQA_VR_DIV 1
+#endif
+#ifndef GQA_PV_RD
+#define GQA_PV_RD 0
+#endif
 
+#ifndef GQA_NW
+#define GQA_NW 4
+#endif
+constexpr int NW = GQA_NW;          // wavefronts per workgroup (32 query rows each)
+constexpr int BM = 32 * NW;         // packed query rows per workgroup
+constexpr int NTHREADS = 64 * NW;
+
+// K and V tiles live in LDS as unpadded row-major [key][d] bf16, filled by
+// direct global->LDS loads (global_load_lds_dwordx4: one wavefront
+// instruction writes 64 x 16 contiguous bytes). Bank conflicts are avoided by
+// an XOR swizzle of the 16-byte chunk index within each row: chunk c of row r
+// sits in slot c ^ swz(r). The K swizzle spreads the 32 rows read by one
+// matrix-core operand load over all banks; the V swizzle does the same for
+// the 4-row x 32-byte footprint of each transposing read.
 template <int D>
 struct Cfg {
-    static constexpr int KS = D + 8;    // LDS row stride of K (elements): conflict-free b128 reads
-    static constexpr int VS = D + 32;   // LDS row stride of V (elements): conflict-free tr16 reads
-    static constexpr int NKL = BN * D / 8 / NTHREADS;  // 16-byte chunks per thread per tensor
+    // keys per tile: 64 at d = 64; 32 at d = 128 keeps two score tiles, the
+    // output accumulator and the Q fragment within 256 VGPRs (2 waves/SIMD).
+    static constexpr int BN = D == 128 ? GQA_BN128 : 64;
+    static constexpr int C8 = D / 8;                    // 16-byte chunks per row
+    static constexpr int NDMA = BN * D * 2 / 1024 / NW;  // DMA instructions per wave per tensor
+    static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+    static __device__ __forceinline__ int swz_v(int r) {
+        return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+    }
 };
 
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(FwdParams p) {
-    constexpr int KS = Cfg<D>::KS, VS = Cfg<D>::VS, NKL = Cfg<D>::NKL;
+    using CF = Cfg<D>;
+    constexpr int BN = CF::BN, C8 = CF::C8, NDMA = CF::NDMA;
     constexpr int DSTEPS = D / 16;  // k-steps of the score product
     constexpr int DBLK = D / 32;    // 32-row blocks of O^T
     constexpr int KB = BN / 32;     // 32-key blocks per tile
-    constexpr int C8 = D / 8;       // 16-byte chunks per K/V row
 
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[2][BN * KS];
-    __shared__ __attribute__((aligned(16))) __bf16 Vs[2][BN * VS];
+    // A 4-slot LDS ring per tensor (tile j in slot j % 4), one array per slot
+    // so that DMA in flight into one slot is visibly disjoint from reads of
+    // another; slot indices are compile-time constants in every step.
+    __shared__ __attribute__((aligned(1024))) __bf16 Ks0[BN * D];
+    __shared__ __attribute__((aligned(1024))) __bf16 Ks1[BN * D];
+    __shared__ __attribute__((aligned(1024))) __bf16 Ks2[BN * D];
+    __shared__ __attribute__((aligned(1024))) __bf16 Ks3[BN * D];
+    __shared__ __attribute__((aligned(1024))) __bf16 Vs0[BN * D];
+    __shared__ __attribute__((aligned(1024))) __bf16 Vs1[BN * D];
+    __shared__ __attribute__((aligned(1024))) __bf16 Vs2[BN * D];
+    __shared__ __attribute__((aligned(1024))) __bf16 Vs3[BN * D];
+    auto kslot = [&](auto j) -> __bf16 * {
+        constexpr int J = decltype(j)::value & 3;
+        return J == 0 ? Ks0 : J == 1 ? Ks1 : J == 2 ? Ks2 : Ks3;
+    };
+    auto vslot = [&](auto j) -> __bf16 * {
+        constexpr int J = decltype(j)::value & 3;
+        return J == 0 ? Vs0 : J == 1 ? Vs1 : J == 2 ? Vs2 : Vs3;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -133,161 +184,264 @@ __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2))) v
     // ---- Q fragment (B operand of S^T = K Q^T), kept in registers ----
     bf16x8 qf[DSTEPS];
     {
+        // rows past the end read the last valid row and are zeroed
+        const int qpos = row_ok ? pos : Lq - 1;
+        const int qhead = row_ok ? head : qh0;
         const __bf16 *qrow =
-            (const __bf16 *)p.q + ((int64_t)(q_tok0 + pos) * p.Hq + head) * D + 8 * half;
+            (const __bf16 *)p.q + ((int64_t)(q_tok0 + qpos) * p.Hq + qhead) * D + 8 * half;
 #pragma unroll
         for (int s = 0; s < DSTEPS; ++s) {
-            if (row_ok) {
-                qf[s] = *(const bf16x8 *)(qrow + 16 * s);
-            } else {
-                qf[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-            }
+            const u32x4 w = *(const u32x4 *)(qrow + 16 * s);
+            qf[s] = __builtin_bit_cast(bf16x8, row_ok ? w : u32x4{0u, 0u, 0u, 0u});
         }
+    }
+
+    // Consume the Q loads before any DMA is issued: the compiler then waits for
+    // them here, instead of at their first use inside the loop, where its
+    // vmcnt wait would also drain the DMA queue.
+    {
+        u32x4 x = __builtin_bit_cast(u32x4, qf[0]);
+#pragma unroll
+        for (int s = 1; s < DSTEPS; ++s) x ^= __builtin_bit_cast(u32x4, qf[s]);
+        asm volatile("" ::"v"(x[0] ^ x[1] ^ x[2] ^ x[3]));
     }
 
     const int64_t kv_stride = (int64_t)p.Hkv * D;
     const __bf16 *kbase = (const __bf16 *)p.k + ((int64_t)k_tok0 * p.Hkv + kvh) * D;
     const __bf16 *vbase = (const __bf16 *)p.v + ((int64_t)k_tok0 * p.Hkv + kvh) * D;
 
-    // Tile staging: thread tid moves 16-byte chunks tid + 256 i (row-major,
-    // D/8 chunks per row) of K and of V. Offsets are fixed per thread.
-    int g_off[NKL], k_soff[NKL], v_soff[NKL], row_of[NKL];
+    // DMA staging: instruction i of wave w fills LDS bytes [1024 (w + NW i), +1024)
+    // of a tile; lane l of it covers chunk slot (64 (w + NW i) + l) % C8 of row
+    // (64 (w + NW i) + l) / C8 and fetches the global chunk that belongs there.
+    int dma_row[NDMA], dma_kc[NDMA], dma_vc[NDMA];
 #pragma unroll
-    for (int i = 0; i < NKL; ++i) {
-        const int c = tid + NTHREADS * i;
-        row_of[i] = c / C8;
-        g_off[i] = (c % C8) * 8;
-        k_soff[i] = row_of[i] * KS + g_off[i];
-        v_soff[i] = row_of[i] * VS + g_off[i];
+    for (int i = 0; i < NDMA; ++i) {
+        const int idx = 64 * (wave + NW * i) + lane;
+        dma_row[i] = idx / C8;
+        dma_kc[i] = ((idx % C8) ^ CF::swz_k(dma_row[i])) * 8;
+        dma_vc[i] = ((idx % C8) ^ CF::swz_v(dma_row[i])) * 8;
     }
-    u32x4 kreg[NKL], vreg[NKL];
-
     // Rows past kend are clamped to the last needed key: they are real, finite
     // K/V rows, their scores are masked to -inf and their p is exactly 0.
-    auto load_tile = [&](int t) {
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto dma_k = [&](int t, __bf16 *dst) {
 #pragma unroll
-        for (int i = 0; i < NKL; ++i) {
-            const int64_t off = (int64_t)min(t * BN + row_of[i], kend - 1) * kv_stride + g_off[i];
-            kreg[i] = *(const u32x4 *)(kbase + off);
-            vreg[i] = *(const u32x4 *)(vbase + off);
+        for (int i = 0; i < NDMA; ++i) {
+            const __bf16 *src =
+                kbase + (int64_t)min(t * BN + dma_row[i], kend - 1) * kv_stride + dma_kc[i];
+            lds_dma16(src, lds_addr(dst) + 1024 * (wave_u + NW * i));
         }
     };
-    auto store_tile = [&](int buf) {
+    auto dma_v = [&](int t, __bf16 *dst) {
 #pragma unroll
-        for (int i = 0; i < NKL; ++i) {
-            *(u32x4 *)(&Ks[buf][k_soff[i]]) = kreg[i];
-            *(u32x4 *)(&Vs[buf][v_soff[i]]) = vreg[i];
+        for (int i = 0; i < NDMA; ++i) {
+            const __bf16 *src =
+                vbase + (int64_t)min(t * BN + dma_row[i], kend - 1) * kv_stride + dma_vc[i];
+            lds_dma16(src, lds_addr(dst) + 1024 * (wave_u + NW * i));
         }
     };
+    // Barrier that lets the two most recent DMA groups (2 x 2 NDMA loads per
+    // wave) stay in flight: everything older has landed in LDS for this wave,
+    // and after s_barrier for every wave. No release fence (which would drain
+    // all outstanding loads); the asm is a compiler memory barrier.
+    static_assert(NDMA == 1 || NDMA == 2, "barrier wait count assumes 1 or 2 DMA loads per tensor");
+    auto barrier_keep2 = [] {
+        if constexpr (NDMA == 2)
+            asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    auto barrier_lds = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
+    // K operand (A of S^T = K Q^T): row kb*32 + col, chunk 2 s + half.
+    int k_rd[DSTEPS];
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s) k_rd[s] = col * D + (((2 * s + half) ^ CF::swz_k(col)) * 8);
     // V^T operand through ds_read_b64_tr_b16: in 16-lane group g, lane j reads
     // row key0 + j/4, columns d0 + 4 (j%4) .. +3 and receives column d0 + j of
     // rows key0 .. key0+3, with d0 = 32 i + 16 (g & 1) and key0 = 4 (g >> 1)
     // (+ 8 for the second read) inside the 16-key slot.
     const int vj = lane & 15, vg = lane >> 4;
-    const int v_rd = (4 * (vg >> 1) + (vj >> 2)) * VS + 16 * (vg & 1) + 4 * (vj & 3);
-    const int k_rd = col * KS + 8 * half;
+    const int v_row = 4 * (vg >> 1) + (vj >> 2);
+    int v_rd[DBLK];
+#pragma unroll
+    for (int i = 0; i < DBLK; ++i) {
+        const int chunk = 4 * i + 2 * (vg & 1) + ((vj & 3) >> 1);
+        v_rd[i] = v_row * D + ((chunk ^ CF::swz_v(v_row)) * 8) + 4 * (vj & 1);
+    }
 
     const float c = p.scale_log2;
-    float m_run = -INFINITY;  // running max of scaled scores, log2 units
+    float m_run = -INFINITY;  // reference max of scaled scores, log2 units
     float l_run = 0.f;        // this lane's share of the running sum
     f32x16 oacc[DBLK];
 #pragma unroll
     for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
 
-    if (ntiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int cur = t & 1;
-        const bool has_next = t + 1 < ntiles;
-        if (has_next) load_tile(t + 1);
-
-        if (wave_live && t * BN < wave_kend) {
-            const __bf16 *ks = Ks[cur];
-            const __bf16 *vs = Vs[cur];
-
-            // S^T tile: rows = keys, columns = this wave's 32 query rows.
-            f32x16 sacc[KB];
+    // S^T tile (rows = keys, columns = this wave's 32 query rows) from LDS.
+    auto scores = [&](const __bf16 *ks, f32x16 (&sacc)[KB]) {
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                sacc[kb] = f32x16{};
-                const __bf16 *krow = ks + kb * 32 * KS + k_rd;
+        for (int kb = 0; kb < KB; ++kb) {
+            sacc[kb] = f32x16{};
 #pragma unroll
-                for (int s = 0; s < DSTEPS; ++s) {
-                    const bf16x8 a = *(const bf16x8 *)(krow + 16 * s);
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
-                }
+            for (int s = 0; s < DSTEPS; ++s) {
+                const bf16x8 a = *(const bf16x8 *)(ks + kb * 32 * D + k_rd[s]);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
             }
-
-            // Element mask only on tiles crossing the diagonal or the end.
-            if ((t + 1) * BN > wave_kfull) {
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = t * BN + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                        if (key >= row_kend) sacc[kb][r] = -INFINITY;
-                    }
-            }
-
-            // Online softmax (running max, rescale, exponentials).
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-            mx = pair_max32(mx);
-            // The reference max only moves when the tile max exceeds it by more
-            // than kRescaleGap (log2 units); every p then stays <= 2^kRescaleGap
-            // and the rescale of O~ is skipped on almost every tile. The result
-            // is the same: m cancels between O~ and l and is added back in L.
-            const float mxs = mx * c;
-            if (mxs > m_run + kRescaleGap) {
-                const float alpha = fast_exp2(m_run - mxs);
-                m_run = mxs;
-                l_run *= alpha;
-#pragma unroll
-                for (int i = 0; i < DBLK; ++i)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-            }
-            const float m_use = m_run == -INFINITY ? 0.f : m_run;
-
-            bf16x8 pf[KB][2];
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float pv = fast_exp2(fmaf(sacc[kb][8 * h2 + j], c, -m_use));
-                        l_run += pv;
-                        pf[kb][h2][j] = (__bf16)pv;
-                    }
-
-            // O^T += V^T P^T. P^T key order in lane (col, half) for k-slot j:
-            // key = kb*32 + 16*h2 + 8*(j/4) + 4*half + j%4, matched by the V^T reads.
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                    for (int i = 0; i < DBLK; ++i) {
-                        const __bf16 *vp = vs + (kb * 32 + 16 * h2) * VS + 32 * i + v_rd;
-                        const u32x2 lo = lds_read_tr16(vp);
-                        const u32x2 hi = lds_read_tr16(vp + 8 * VS);
-                        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-                        oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][h2], oacc[i], 0, 0, 0);
-                    }
         }
+    };
+    // Element mask (only on tiles crossing the diagonal or the end), then the
+    // tile's row max and the reference-max update with the rare rescale of O~.
+    auto mask_and_max = [&](int t, f32x16 (&sacc)[KB]) {
+        if ((t + 1) * BN > wave_kfull) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = t * BN + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    if (key >= row_kend) sacc[kb][r] = -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+        mx = pair_max32(mx);
+        // The reference max only moves when the tile max exceeds it by more
+        // than kRescaleGap (log2 units); every p then stays <= 2^kRescaleGap
+        // and the rescale of O~ is skipped on almost every tile. The result
+        // is the same: m cancels between O~ and l and is added back in L.
+        const float mxs = mx * c;
+        if (mxs > m_run + kRescaleGap) {
+            const float alpha = fast_exp2(m_run - mxs);
+            m_run = mxs;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+        }
+    };
+    // p = 2^(s c - m) in fp32 (summed into l), rounded to bf16 as the B operand.
+    auto probs = [&](const f32x16 (&sacc)[KB], bf16x8 (&pf)[KB][2]) {
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float pv = fast_exp2(fmaf(sacc[kb][8 * h2 + j], c, -m_use));
+                    l_run += pv;
+                    pf[kb][h2][j] = (__bf16)pv;
+                }
+    };
+    // O^T += V^T P^T. P^T key order in lane (col, half) for k-slot j:
+    // key = kb*32 + 16*h2 + 8*(j/4) + 4*half + j%4, matched by the V^T reads.
+    auto accumulate = [&](const __bf16 *vs, const bf16x8 (&pf)[KB][2]) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < DBLK; ++i) {
+                    const __bf16 *vp = vs + (kb * 32 + 16 * h2) * D + v_rd[i];
+                    const u32x2 lo = lds_read_tr16(vp);
+                    const u32x2 hi = lds_read_tr16(vp + 8 * D);
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                    oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][h2], oacc[i], 0, 0, 0);
+                }
+    };
+    auto wave_needs = [&](int t) { return wave_live && t < ntiles && t * BN < wave_kend; };
 
-        if (has_next) store_tile(cur ^ 1);
-        __syncthreads();
+    // Software pipeline, one barrier per tile, DMA three tiles ahead.
+    // Entering step t: K(t+1) and V(t) have landed in LDS, the DMA of K(t+2),
+    // K(t+3), V(t+1), V(t+2) may be in flight, and the scores of tile t are
+    // masked with the reference max updated. Step t starts the DMA of K(t+4)
+    // (into K(t)'s slot) and V(t+3) (into V(t-1)'s slot), computes the scores
+    // of tile t+1 on the matrix cores while the vector units turn tile t into
+    // probabilities, accumulates P(t) V(t), then waits until K(t+2) and
+    // V(t+1) have landed and meets the other waves. Tiles past the end are
+    // loaded from the clamped last row (never used) so that every step issues
+    // the same number of DMA loads and the wait count stays exact.
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    f32x16 sa[KB], sb[KB];
+    if (ntiles > 0) {
+        dma_k(0, kslot(I0{}));
+        dma_k(1, kslot(I1{}));
+        dma_v(0, vslot(I0{}));
+        dma_k(2, kslot(I2{}));
+        dma_v(1, vslot(I1{}));
+        dma_k(3, kslot(I3{}));
+        dma_v(2, vslot(I2{}));
+        barrier_keep2();  // K(0), K(1), V(0) have landed
+        if (wave_needs(0)) {
+            scores(kslot(I0{}), sa);
+            mask_and_max(0, sa);
+        }
+        barrier_lds();  // K(0)'s slot is refilled with K(4) in step 0
     }
+
+    auto step = [&](auto jc, int t, f32x16(&s_cur)[KB], f32x16(&s_nxt)[KB]) {
+        constexpr int J = decltype(jc)::value;
+        __bf16 *k_next = kslot(std::integral_constant<int, J + 1>{});  // K(t+1)
+        __bf16 *v_cur = vslot(std::integral_constant<int, J>{});       // V(t)
+        const bool do_t = wave_needs(t), do_n = wave_needs(t + 1);
+        dma_k(t + 4, kslot(std::integral_constant<int, J>{}));
+        dma_v(t + 3, vslot(std::integral_constant<int, J + 3>{}));
+        bf16x8 pf[KB][2];
+        if (do_t && do_n) {
+            scores(k_next, s_nxt);
+            probs(s_cur, pf);
+            accumulate(v_cur, pf);
+            // Interleave: each score MFMA of tile t+1 is followed by a slice of
+            // tile t's exponentials and the LDS reads for the next products,
+            // so the vector units work while the matrix cores run.
+            constexpr int NSM = KB * DSTEPS;    // score MFMAs
+            constexpr int NPM = KB * 2 * DBLK;  // P.V MFMAs
+            constexpr int NVR = 2 * NPM;        // transposing V reads
+            constexpr int VALU_PER = (KB * 16 * 7 / 2 + NSM - 1) / NSM;
+            // LDS operand reads run GQA_PF_K score-MFMAs ahead of their use;
+            // V reads are spread over the score phase so that the P.V MFMAs
+            // find their operands in registers.
+            __builtin_amdgcn_sched_group_barrier(0x100, GQA_PF_K, 0);
+#pragma unroll
+            for (int g = 0; g < NSM; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (scores)
+                __builtin_amdgcn_sched_group_barrier(0x100, 1 + NVR / NSM / GQA_VR_DIV, 0);  // DS reads
+                __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER, 0);  // VALU (exp)
+            }
+#pragma unroll
+            for (int g = 0; g < NPM; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x100, GQA_PV_RD, 0);  // DS reads (V)
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (P.V)
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+            }
+        } else {
+            if (do_n) scores(k_next, s_nxt);
+            if (do_t) {
+                probs(s_cur, pf);
+                accumulate(v_cur, pf);
+            }
+        }
+        if (do_n) mask_and_max(t + 1, s_nxt);
+        barrier_keep2();
+    };
+    int t = 0;
+    for (; t + 3 < ntiles; t += 4) {
+        step(I0{}, t, sa, sb);
+        step(I1{}, t + 1, sb, sa);
+        step(I2{}, t + 2, sa, sb);
+        step(I3{}, t + 3, sb, sa);
+    }
+    if (t < ntiles) step(I0{}, t, sa, sb);
+    if (t + 1 < ntiles) step(I1{}, t + 1, sb, sa);
+    if (t + 2 < ntiles) step(I2{}, t + 2, sa, sb);
+    // drain this wave's remaining (unused) DMA before the workgroup can end
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue: one division by l, L = m + log(l) ----
     const float l_tot = pair_sum32(l_run);
