@@ -82,35 +82,26 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
-class Timer:
-    """Per-launch HIP-event timing on the launch stream."""
-
-    def __init__(self, torch, n):
-        self.torch = torch
-        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(n)]
-
-    def avg_ms(self):
-        ts = [a.elapsed_time(b) for a, b in self.ev]
-        return sum(ts) / len(ts), min(ts)
-
-
 def run_timed(torch, step, steps, warmup):
-    """W untimed steps, then exactly K timed steps between two synchronisations."""
+    """W untimed steps, then exactly K timed steps between two synchronisations.
+
+    Two HIP events on the launch stream (torch's current stream, which the
+    binding passes to the library) bracket the K launches; their elapsed time
+    / K is the average launch duration. Returns (wall seconds, average ms).
+    """
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    tm = Timer(torch, steps)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    start.record()
     for i in range(steps):
-        a, b = tm.ev[i]
-        a.record()
         step(i)
-        b.record()
+    end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    avg, mn = tm.avg_ms()
-    return wall, avg, mn
+    return wall, start.elapsed_time(end) / steps
 
 
 def to_device(torch, w, sets):
@@ -153,7 +144,7 @@ def bench_fwd(torch, ga, w, steps, warmup, sets):
     def step(i):
         plans[i % sets].run()
 
-    wall, avg_ms, min_ms = run_timed(torch, step, steps, warmup)
+    wall, avg_ms = run_timed(torch, step, steps, warmup)
     if w.varlen:
         cu = w.cu_seqlens_q.tolist()
         flops = sum(fwd_flops(cu[b + 1] - cu[b], cu[b + 1] - cu[b], w.q.shape[1], w.q.shape[2],
@@ -161,7 +152,7 @@ def bench_fwd(torch, ga, w, steps, warmup, sets):
     else:
         B, S, H, d = w.q.shape
         flops = B * fwd_flops(S, w.k.shape[1], H, d, w.causal)
-    return dict(flops=flops, wall=wall, avg_ms=avg_ms, min_ms=min_ms)
+    return dict(flops=flops, wall=wall, avg_ms=avg_ms)
 
 
 def bench_decode(torch, ga, w, ns, steps, warmup, sets):
@@ -179,9 +170,9 @@ def bench_decode(torch, ga, w, ns, steps, warmup, sets):
     def step(i):
         plans[i % sets].run()
 
-    wall, avg_ms, min_ms = run_timed(torch, step, steps, warmup)
+    wall, avg_ms = run_timed(torch, step, steps, warmup)
     kv_bytes = 2 * w.k.numel() * w.k.element_size()
-    return dict(bytes=kv_bytes, wall=wall, avg_ms=avg_ms, min_ms=min_ms)
+    return dict(bytes=kv_bytes, wall=wall, avg_ms=avg_ms)
 
 
 def cpu_baseline(w, budget_s=15.0):
@@ -209,6 +200,69 @@ def cpu_baseline(w, budget_s=15.0):
                       f"{el:.1f} s"}
 
 
+def summarize_counters(pmc_dir: str, out_path: str) -> dict:
+    """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs into HBM bytes per launch.
+
+    Expects <pmc_dir>/copy_fetch, copy_write (gqa_attention_amd/hbm_probe
+    268435456: one copy of 256 MiB read + 256 MiB written, and a 256 MiB read
+    stream) and <workload>_fetch, <workload>_write directories (bench.py
+    --workload <workload>). Each counter is scaled by the ratio between the
+    copy kernel's known bytes and what the same counter reports for it.
+    """
+    import csv
+    import glob
+    import statistics
+
+    def read(name):
+        files = glob.glob(os.path.join(pmc_dir, name, "*_counter_collection.csv"))
+        per_kernel = {}
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                per_kernel.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return per_kernel
+
+    copy_bytes = 268435456
+    fetch = read("copy_fetch")
+    write = read("copy_write")
+    kf = [v for k, v in fetch.items() if k.startswith("copy_kernel")][0]
+    kw = [v for k, v in write.items() if k.startswith("copy_kernel")][0]
+    scale_fetch = copy_bytes / (statistics.mean(kf) * 1024)
+    scale_write = copy_bytes / (statistics.mean(kw) * 1024)
+    out = {"_scale": {"fetch_size_bytes_per_kib": scale_fetch * 1024,
+                      "write_size_bytes_per_kib": scale_write * 1024,
+                      "reference": "copy_kernel of gqa_attention_amd/hbm_probe, 256 MiB read + 256 MiB "
+                                   "written per launch"}}
+    kernels = {"fwd_bf16_kernel": "fwd_bf16", "decode_bf16_kernel": "decode_bf16"}
+    for d in sorted(glob.glob(os.path.join(pmc_dir, "*_fetch"))):
+        wl = os.path.basename(d)[:-len("_fetch")]
+        if wl == "copy":
+            continue
+        f, w = read(wl + "_fetch"), read(wl + "_write")
+        for kname, vals in f.items():
+            tag = next((v for k, v in kernels.items() if k in kname), None)
+            if tag is None or kname not in w:
+                continue
+            fb = statistics.mean(vals) * 1024 * scale_fetch
+            wb = statistics.mean(w[kname]) * 1024 * scale_write
+            out[f"{tag}:{WORKLOAD_NAMES[wl]}"] = {
+                "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+                "bytes_per_launch": round(fb + wb), "kernel": kname[:120],
+                "source_digest": source_digest(KERNEL_SOURCES[tag]),
+                "command": f"rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python3 bench.py "
+                           f"--workload {wl} --steps 3 --warmup 1 --no-extra --no-cpu-baseline"}
+    with open(out_path, "w") as fh:
+        json.dump(out, fh, indent=1, sort_keys=True)
+    return out
+
+
+WORKLOAD_NAMES = {
+    "bert_base_encoder": "bert_base_encoder_b64_s512_h12_d64",
+    "llama31_8b_prefill": "llama31_8b_prefill_s8192_h32_kv8_d128",
+    "llama31_8b_decode": "llama31_8b_decode_b64_kv4096_h32_kv8_d128",
+    "varlen_packed_causal": "varlen_packed_causal_h48_kv12_d128_n32",
+}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -220,7 +274,15 @@ def main():
     ap.add_argument("--num-splits", type=int, default=1, help="decode workload only")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-counters", metavar="PMC_DIR",
+                    help="write profiles/hbm_traffic.json from rocprofv3 counter runs and exit")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        res = summarize_counters(args.summarize_counters,
+                                 os.path.join(ROOT, "profiles", "hbm_traffic.json"))
+        print(json.dumps(res, indent=1))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
@@ -242,7 +304,7 @@ def main():
         peak = PEAK_BF16_TFLOPS if w.q.dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
         return r, {"workload": w.name, "kernel": "fwd_bf16" if w.q.dtype == torch.bfloat16
                    else "fwd_f32", "tflops": round(tf, 2), "frac_peak": round(tf / peak, 4),
-                   "ms_per_launch": round(r["avg_ms"], 5), "min_ms": round(r["min_ms"], 5),
+                   "ms_per_launch": round(r["avg_ms"], 5),
                    "gflop": round(r["flops"] / 1e9, 3)}
 
     loaders = {
