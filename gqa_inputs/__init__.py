@@ -16,7 +16,8 @@ Recipe (every tensor is i.i.d. N(0, 1)):
 
 Layouts: fixed length ``[B, S, H, d]`` (batch, sequence, head, head_dim);
 variable length ``[T, H, d]`` with int32 ``cu_seqlens`` of length B+1;
-decode ``q [B, Hq, d]`` with a cache ``[B, Sk, Hkv, d]``.
+decode ``q [B, Hq, d]`` with a cache ``[B, Sk, Hkv, d]``; general-cache decode
+(``CacheWorkload``) with a contiguous or paged cache and per-sequence lengths.
 
 The five named workloads take their shapes from the pages: the GQA snippet of
 the Ultralytics glossary page "Grouped Query Attention (GQA)" (8 query heads,
@@ -99,6 +100,102 @@ def decode(B: int, Hq: int, Hkv: int, Sk: int, d: int, *, seed: int,
                     decode=True)
 
 
+# Stored value of cache slots that no sequence owns (the tail of a sequence's
+# last page, the tail of a contiguous cache row, the spare page that unused
+# block-table entries point to). Exactly representable in bf16 and e4m3; large
+# enough that attending to it by mistake changes the result visibly.
+POISON = 16.0
+
+
+@dataclass
+class CacheWorkload:
+    """Decode against a general K/V cache (per-sequence lengths, optional
+    paging, sliding window, bf16 or fp8 e4m3 storage). CPU tensors."""
+
+    name: str
+    q: torch.Tensor                       # [B, Hq, d] bf16
+    k_cache: torch.Tensor                 # [B, S, Hkv, d] or [pages, block_size, Hkv, d]
+    v_cache: torch.Tensor
+    seqlens: Optional[torch.Tensor]       # int32 [B], None: every sequence holds S keys
+    block_table: Optional[torch.Tensor]   # int32 [B, blocks_per_seq], None: contiguous
+    block_size: int                       # 0 for a contiguous cache
+    max_seqlen_k: int
+    window_left: int                      # -1: no window
+    k_scale: float                        # dequantisation scales (1 for bf16)
+    v_scale: float
+    scale: float
+
+    @property
+    def fp8(self) -> bool:
+        return self.k_cache.dtype == torch.float8_e4m3fn
+
+    @property
+    def batch(self) -> int:
+        return self.q.shape[0]
+
+    def lengths(self):
+        if self.seqlens is None:
+            return [self.max_seqlen_k] * self.batch
+        return [int(x) for x in self.seqlens.tolist()]
+
+
+def cache_decode(lengths, Hq: int, Hkv: int, d: int, *, seed: int, block_size: int = 0,
+                 window_left: int = -1, fp8: bool = False, k_scale: float = 1.0,
+                 v_scale: float = 1.0, with_seqlens: bool = True,
+                 scale: Optional[float] = None, name: str = "cache_decode") -> CacheWorkload:
+    """q [B, Hq, d] bf16 and a K/V cache holding lengths[b] keys of sequence b.
+
+    Draw order: q, then the page permutation (paged only), then k, then v.
+    Contiguous (block_size 0): caches [B, max(lengths), Hkv, d]. Paged: each
+    sequence gets ceil(L / block_size) pages taken from a random permutation
+    of all pages; one extra page is left unowned; caches
+    [pages, block_size, Hkv, d], block table int32 [B, ceil(max L / block_size)]
+    with every unused entry naming the unowned page. Stored values are
+    N(0, 1) rounded to bf16, or to e4m3 (``.to(torch.float8_e4m3fn)``) when
+    fp8; unowned slots hold POISON. ``with_seqlens=False`` (all lengths
+    equal) gives no length array.
+    """
+    lens = [int(x) for x in lengths]
+    if not with_seqlens and len(set(lens)) != 1:
+        raise ValueError("with_seqlens=False needs equal lengths")
+    B = len(lens)
+    S = max(max(lens), 1)
+    g = torch.Generator().manual_seed(seed)
+    q = _randn(g, (B, Hq, d), torch.bfloat16)
+    if block_size == 0:
+        k = torch.randn(B, S, Hkv, d, generator=g)
+        v = torch.randn(B, S, Hkv, d, generator=g)
+        for b, L in enumerate(lens):
+            k[b, L:] = POISON
+            v[b, L:] = POISON
+        table = None
+    else:
+        nblk = -(-S // block_size)
+        used = [-(-L // block_size) for L in lens]
+        n_pages = sum(used) + 1
+        perm = torch.randperm(n_pages, generator=g).tolist()
+        spare = perm[-1]
+        table = torch.full((B, nblk), spare, dtype=torch.int32)
+        k = torch.randn(n_pages, block_size, Hkv, d, generator=g)
+        v = torch.randn(n_pages, block_size, Hkv, d, generator=g)
+        k[spare] = POISON
+        v[spare] = POISON
+        at = 0
+        for b, L in enumerate(lens):
+            pages = perm[at:at + used[b]]
+            at += used[b]
+            table[b, :used[b]] = torch.tensor(pages, dtype=torch.int32)
+            if used[b] and L % block_size:
+                k[pages[-1], L % block_size:] = POISON
+                v[pages[-1], L % block_size:] = POISON
+    dt = torch.float8_e4m3fn if fp8 else torch.bfloat16
+    k, v = k.to(dt), v.to(dt)
+    seqlens = torch.tensor(lens, dtype=torch.int32) if with_seqlens else None
+    return CacheWorkload(name, q, k, v, seqlens, table, block_size, S, window_left,
+                         k_scale if fp8 else 1.0, v_scale if fp8 else 1.0,
+                         d ** -0.5 if scale is None else scale)
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads.
 # ---------------------------------------------------------------------------
@@ -150,6 +247,35 @@ def varlen_packed_causal_48_12() -> Workload:
     cu = torch.tensor([0] + lengths, dtype=torch.int64).cumsum(0).to(torch.int32)
     return Workload("varlen_packed_causal_h48_kv12_d128_n32", q, k, v, True,
                     128 ** -0.5, cu, cu.clone(), max(lengths), max(lengths))
+
+
+def llama31_8b_decode_ragged_paged(fp8: bool = False) -> CacheWorkload:
+    """Decode over a paged cache of ragged lengths: B 64, 32 query / 8 KV
+    heads, d 128, cache lengths uniform on [1, 8192] (drawn first from seed 6),
+    16-key pages; bf16, or e4m3 with k_scale 0.25 and v_scale 0.5."""
+    g = torch.Generator().manual_seed(6)
+    lengths = torch.randint(1, 8193, (64,), generator=g).tolist()
+    tag = "fp8" if fp8 else "bf16"
+    return cache_decode(lengths, 32, 8, 128, seed=7, block_size=16, fp8=fp8,
+                        k_scale=0.25, v_scale=0.5,
+                        name=f"llama31_8b_decode_ragged_paged16_{tag}_b64_h32_kv8_d128")
+
+
+def sliding_window_decode() -> CacheWorkload:
+    """Sliding-window decode (window of 4096 keys, as Mistral 7B pairs with
+    GQA): B 32, 32 query / 8 KV heads, d 128, cache lengths uniform on
+    [1, 16384] (drawn first from seed 8), 16-key pages, bf16."""
+    g = torch.Generator().manual_seed(8)
+    lengths = torch.randint(1, 16385, (32,), generator=g).tolist()
+    return cache_decode(lengths, 32, 8, 128, seed=9, block_size=16, window_left=4095,
+                        name="sliding_window4096_decode_paged16_b32_h32_kv8_d128")
+
+
+CACHE_NAMED = {
+    "decode_ragged_paged": lambda: llama31_8b_decode_ragged_paged(False),
+    "decode_ragged_paged_fp8": lambda: llama31_8b_decode_ragged_paged(True),
+    "decode_sliding_window": sliding_window_decode,
+}
 
 
 NAMED = {

@@ -8,8 +8,11 @@ Modules:
   gqa        the plain definition (materialised S and P, K/V expanded per head)
   brute      a pure-Python scalar restatement used to pin ``attention``
   kv_cache   KV-cache size arithmetic pinned to the glossary's printed figures
+  cache      decode over a general cache: per-sequence lengths, pages, a
+             sliding window, fp8 (e4m3) storage
 """
 from .gqa import (attention, attention_rows, decode, decode_partials,  # noqa: F401
                         merge_partials, split_ranges, attention_flops, head_rows,
                         expand_kv, kv_head_of, visible, as_f64)
 from .kv_cache import kv_cache_bytes, kv_cache_elements  # noqa: F401
+from .cache import decode_cache, fp8_e4m3_decode  # noqa: F401
