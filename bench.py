@@ -11,11 +11,13 @@ Printed: ONE JSON line with the metric, the dominant kernel's roofline
 (algorithmic flops or bytes per launch / launch time from HIP events on the
 launch stream), the CPU oracle timed on a bounded sample (rank 0, N = 1) and,
 under "extra", the other workloads (8192-token causal GQA prefill, split-KV
-decode at num_splits 1/2/4/8, packed variable-length causal GQA, tiny fp32).
+decode at num_splits 1/2/4/8, packed variable-length causal GQA, tiny fp32,
+and decode over general caches: ragged paged bf16 and fp8, sliding window).
 
 Flop count: 4 * d per visible (query, key) pair per query head (two products,
 multiply-add = 2 flops). Decode bytes: the K and V cache bytes read,
-2 * B * Sk * Hkv * d * 2.
+2 * B * Sk * Hkv * d * 2; for a general cache, the visible keys of every
+sequence x Hkv x d x element size x 2.
 """
 from __future__ import annotations
 
@@ -175,6 +177,28 @@ def bench_decode(torch, ga, w, ns, steps, warmup, sets):
     return dict(bytes=kv_bytes, wall=wall, avg_ms=avg_ms)
 
 
+def cache_kv_bytes(wc) -> int:
+    """K and V bytes a decode over a general cache must read: the visible keys
+    of every sequence x Hkv x d x element size, for K and for V."""
+    hkv, d = wc.k_cache.shape[2], wc.k_cache.shape[3]
+    n = 0
+    for L in wc.lengths():
+        lo = 0 if wc.window_left < 0 else max(0, L - 1 - wc.window_left)
+        n += L - lo
+    return 2 * n * hkv * d * wc.k_cache.element_size()
+
+
+def bench_decode_ex(torch, ga, wc, ns, steps, warmup):
+    q, k, v = wc.q.cuda(), wc.k_cache.cuda(), wc.v_cache.cuda()
+    sl = wc.seqlens.cuda() if wc.seqlens is not None else None
+    bt = wc.block_table.cuda() if wc.block_table is not None else None
+    plan = ga.DecodeExPlan(q, k, v, seqlens_k=sl, block_table=bt, window_left=wc.window_left,
+                           k_scale=wc.k_scale, v_scale=wc.v_scale, scale=wc.scale,
+                           num_splits=ns)
+    wall, avg_ms = run_timed(torch, lambda i: plan.run(), steps, warmup)
+    return dict(bytes=cache_kv_bytes(wc), wall=wall, avg_ms=avg_ms)
+
+
 def cpu_baseline(w, budget_s=15.0):
     """The fp64 oracle as it stands, on the first batches of the workload until
     about `budget_s` seconds of CPU work; reported in the metric's unit."""
@@ -270,7 +294,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="bert_base_encoder",
                     choices=["bert_base_encoder", "llama31_8b_prefill", "llama31_8b_decode",
-                             "varlen_packed_causal", "tiny_causal_gqa_fp32"])
+                             "varlen_packed_causal", "tiny_causal_gqa_fp32",
+                             "decode_ragged_paged", "decode_ragged_paged_fp8",
+                             "decode_sliding_window"])
     ap.add_argument("--num-splits", type=int, default=1, help="decode workload only")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -315,6 +341,34 @@ def main():
         "llama31_8b_decode": gqa_inputs.llama31_8b_decode,
     }
     sets_for = {"bert_base_encoder": 3, "llama31_8b_decode": 2}
+
+    def cache_entry(wc, ns, steps, warmup):
+        rc = bench_decode_ex(torch, ga, wc, ns, steps, warmup)
+        gbs = rc["bytes"] / (rc["avg_ms"] * 1e-3) / 1e9
+        kern = "decode_bf16" + ("+combine" if ns > 1 else "")
+        return rc, {"workload": wc.name, "kernel": kern, "num_splits": ns,
+                    "kv_gbs": round(gbs, 1), "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
+                    "ms_per_call": round(rc["avg_ms"], 5), "kv_bytes": rc["bytes"]}
+
+    if args.workload in gqa_inputs.CACHE_NAMED:
+        w = gqa_inputs.CACHE_NAMED[args.workload]()
+        r, e = cache_entry(w, args.num_splits, args.steps, args.warmup)
+        gbs = e["kv_gbs"]
+        line = {"metric": METRIC, "value": round(r["bytes"] * args.steps / r["wall"] / 1e9, 3),
+                "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": round(r["wall"] * 1e3 / args.steps, 5),
+                "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                "dtype": "fp8_e4m3" if w.fp8 else "bf16", "data": "synthetic",
+                "config": {"workload": w.name, "B": w.batch, "Hq": w.q.shape[1],
+                           "Hkv": w.k_cache.shape[2], "d": w.q.shape[2],
+                           "block_size": w.block_size, "window_left": w.window_left,
+                           "num_splits": args.num_splits, "kv_bytes": r["bytes"]},
+                "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                             "traffic": measured_traffic("decode_bf16", w.name),
+                             "kernel": e["kernel"], "launch_ms": e["ms_per_call"]}}
+        print(json.dumps(line))
+        return
 
     w = loaders[args.workload]()
     sets = sets_for.get(args.workload, 1)
@@ -382,6 +436,13 @@ def main():
                               "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
                               "ms_per_call": round(rd["avg_ms"], 5)})
             del wd
+        for cname in sorted(gqa_inputs.CACHE_NAMED):
+            wc = gqa_inputs.CACHE_NAMED[cname]()
+            for ns in (1, 2, 4, 8):
+                _, e = cache_entry(wc, ns, 20, 3)
+                extra.append(e)
+            del wc
+            torch.cuda.empty_cache()
         line["extra"] = extra
 
     if not args.no_cpu_baseline and not w.decode:

@@ -12,9 +12,12 @@ Functions mirror the C entry points:
   max_seqlen_q=None, max_seqlen_k=None)`` -> ``(out, lse)``
 * ``decode(q, k_cache, v_cache, scale=None, num_splits=1, workspace=None)`` ->
   ``(out, lse)``
+* ``decode_ex(q, k_cache, v_cache, seqlens_k=None, block_table=None,
+  window_left=-1, k_scale=1.0, v_scale=1.0, ...)`` -> ``(out, lse)``: decode
+  over a ragged, paged, windowed, bf16 or fp8 e4m3 cache
 * ``decode_workspace_bytes(B, Hq, d, num_splits)``
-* ``FwdPlan`` / ``DecodePlan``: the same calls marshalled once, re-issued by
-  ``run()`` (for loops over fixed shapes and buffers)
+* ``FwdPlan`` / ``DecodePlan`` / ``DecodeExPlan``: the same calls marshalled
+  once, re-issued by ``run()`` (for loops over fixed shapes and buffers)
 * ``strerror(status)``
 """
 from __future__ import annotations
@@ -26,12 +29,13 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["fwd", "decode", "FwdPlan", "DecodePlan", "decode_workspace_bytes", "strerror", "lib", "library_path",
+__all__ = ["fwd", "decode", "decode_ex", "FwdPlan", "DecodePlan", "DecodeExPlan",
+           "decode_workspace_bytes", "strerror", "lib", "library_path",
            "GQA_OK", "GQA_EINVAL", "GQA_EUNSUPPORTED", "GQA_EWORKSPACE", "GQA_ELAUNCH",
-           "GQA_DTYPE_BF16", "GQA_DTYPE_FP32", "GqaError"]
+           "GQA_DTYPE_BF16", "GQA_DTYPE_FP32", "GQA_DTYPE_FP8_E4M3", "GqaError"]
 
 GQA_OK, GQA_EINVAL, GQA_EUNSUPPORTED, GQA_EWORKSPACE, GQA_ELAUNCH = 0, 1, 2, 3, 4
-GQA_DTYPE_BF16, GQA_DTYPE_FP32 = 0, 1
+GQA_DTYPE_BF16, GQA_DTYPE_FP32, GQA_DTYPE_FP8_E4M3 = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgqa_attn.so")
@@ -67,6 +71,9 @@ def lib() -> ctypes.CDLL:
     L.gqa_attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz,
                                   i32, vp]
     L.gqa_attn_decode.restype = i32
+    L.gqa_attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, i32, vp,
+                                     i32, i32, i32, i32, f32, f32, i32, vp, sz, vp]
+    L.gqa_attn_decode_ex.restype = i32
     L.gqa_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.gqa_attn_decode_workspace_bytes.restype = sz
     L.gqa_attn_strerror.argtypes = [i32]
@@ -281,4 +288,107 @@ class DecodePlan:
         st = self._fn(*self._args, _stream_handle(self._dev))
         if st:
             _raise(st, "gqa_attn_decode")
+        return self.out, self.lse
+
+
+def _prepare_decode_ex(q, k_cache, v_cache, seqlens_k, block_table, max_seqlen_k,
+                       window_left, k_scale, v_scale, scale, num_splits, workspace, out, lse):
+    """Check tensor metadata, allocate outputs / workspace, build the C arguments."""
+    dev = q.device
+    _check("q", q, 3, torch.bfloat16, None)
+    kv_dt = k_cache.dtype
+    if kv_dt == torch.bfloat16:
+        code = GQA_DTYPE_BF16
+    elif kv_dt == torch.float8_e4m3fn:
+        code = GQA_DTYPE_FP8_E4M3
+    else:
+        raise ValueError(f"k_cache dtype {kv_dt}: expected bfloat16 or float8_e4m3fn")
+    _check("k_cache", k_cache, 4, kv_dt, dev)
+    _check("v_cache", v_cache, 4, kv_dt, dev)
+    B, Hq, d = q.shape
+    if k_cache.shape != v_cache.shape or k_cache.shape[-1] != d:
+        raise ValueError("k_cache and v_cache must have the same shape, head_dim as q")
+    Hkv = k_cache.shape[2]
+    if block_table is None:
+        if k_cache.shape[0] != B:
+            raise ValueError("contiguous caches must be [B, max_seqlen_k, Hkv, d]")
+        cap = k_cache.shape[1]
+        if max_seqlen_k is not None and int(max_seqlen_k) != cap:
+            raise ValueError("a contiguous cache's max_seqlen_k is its second dimension")
+        bptr, bsize, nblk = None, 0, 0
+    else:
+        _check("block_table", block_table, 2, torch.int32, dev)
+        if block_table.shape[0] != B:
+            raise ValueError("block_table must be [B, max_blocks_per_seq]")
+        bsize, nblk = k_cache.shape[1], block_table.shape[1]
+        cap = bsize * nblk
+        bptr = block_table.data_ptr()
+    smax = cap if max_seqlen_k is None else int(max_seqlen_k)
+    if seqlens_k is not None:
+        _check("seqlens_k", seqlens_k, 1, torch.int32, dev)
+        if seqlens_k.shape[0] != B:
+            raise ValueError("seqlens_k must be [B]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    _check("out", out, 3, torch.bfloat16, dev)
+    _check("lse", lse, 2, torch.float32, dev)
+    need = decode_workspace_bytes(B, Hq, d, num_splits) if num_splits >= 1 else 0
+    if num_splits > 1 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+            lse.data_ptr(), B, Hq, Hkv, d, sc,
+            seqlens_k.data_ptr() if seqlens_k is not None else None, smax, bptr, bsize, nblk,
+            int(window_left), code, float(k_scale), float(v_scale), int(num_splits), ws_ptr,
+            ws_bytes)
+    return out, lse, workspace, args
+
+
+def decode_ex(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *,
+              seqlens_k: Optional[torch.Tensor] = None,
+              block_table: Optional[torch.Tensor] = None, max_seqlen_k: Optional[int] = None,
+              window_left: int = -1, k_scale: float = 1.0, v_scale: float = 1.0,
+              scale: Optional[float] = None, num_splits: int = 1,
+              workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+              lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Decode through ``gqa_attn_decode_ex`` over a general K/V cache.
+
+    q [B, Hq, d] bf16. Contiguous caches [B, S, Hkv, d]; paged caches
+    [pages, block_size, Hkv, d] with an int32 device ``block_table``
+    [B, max_blocks_per_seq]. Cache dtype bfloat16 or float8_e4m3fn (then
+    ``k_scale`` / ``v_scale`` dequantise). ``seqlens_k`` int32 [B] on the
+    device gives each sequence's key count (None: all hold ``max_seqlen_k``,
+    which defaults to the cache's capacity). ``window_left`` W >= 0 keeps the
+    last W + 1 keys. Returns out [B, Hq, d] bf16, lse fp32 [B, Hq].
+    """
+    out, lse, _, args = _prepare_decode_ex(q, k_cache, v_cache, seqlens_k, block_table,
+                                           max_seqlen_k, window_left, k_scale, v_scale, scale,
+                                           num_splits, workspace, out, lse)
+    with torch.cuda.device(q.device):
+        st = lib().gqa_attn_decode_ex(*args, _stream_handle(q.device))
+    _raise(st, "gqa_attn_decode_ex")
+    return out, lse
+
+
+class DecodeExPlan:
+    """A ``decode_ex`` call checked and marshalled once; ``run()`` re-issues it."""
+
+    def __init__(self, q, k_cache, v_cache, *, seqlens_k=None, block_table=None,
+                 max_seqlen_k=None, window_left=-1, k_scale=1.0, v_scale=1.0, scale=None,
+                 num_splits=1, workspace=None, out=None, lse=None):
+        self.out, self.lse, self.workspace, self._args = _prepare_decode_ex(
+            q, k_cache, v_cache, seqlens_k, block_table, max_seqlen_k, window_left, k_scale,
+            v_scale, scale, num_splits, workspace, out, lse)
+        self._keep = (q, k_cache, v_cache, seqlens_k, block_table)
+        self._dev = q.device
+        self._fn = lib().gqa_attn_decode_ex
+
+    def run(self):
+        st = self._fn(*self._args, _stream_handle(self._dev))
+        if st:
+            _raise(st, "gqa_attn_decode_ex")
         return self.out, self.lse

@@ -120,11 +120,14 @@ int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache, voi
         p.G = Hq / Hkv;
         p.n_qs = (p.G + 15) / 16;
         p.num_splits = num_splits;
-        p.split_chunk = chunk;
         p.scale_log2 = scale * 1.4426950408889634f;
+        p.v_scale = 1.f;
+        p.seqlens = nullptr;
+        p.block_table = nullptr;
+        p.window_left = -1;
         p.ws_o = ws_o;
         p.ws_lse = ws_lse;
-        hipError_t e = gqa::launch_decode_bf16(p, d, s);
+        hipError_t e = gqa::launch_decode_bf16(p, d, false, false, s);
         if (e != hipSuccess || num_splits == 1) return status_from(e);
         return status_from(
             gqa::launch_decode_combine(ws_o, ws_lse, out, lse, rows, num_splits, d, true, s));
@@ -156,6 +159,58 @@ int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache, voi
     if (e != hipSuccess) return status_from(e);
     return status_from(
         gqa::launch_decode_combine(ws_o, ws_lse, out, lse, rows, num_splits, d, false, s));
+}
+
+int gqa_attn_decode_ex(const void *q, const void *k_cache, const void *v_cache, void *out,
+                       float *lse, int B, int Hq, int Hkv, int d, float scale,
+                       const int32_t *seqlens_k, int max_seqlen_k, const int32_t *block_table,
+                       int block_size, int max_blocks_per_seq, int window_left, int kv_dtype,
+                       float k_scale, float v_scale, int num_splits, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    const int rc = gqa::validate_decode_ex(q, k_cache, v_cache, out, lse, B, Hq, Hkv, d, scale,
+                                           seqlens_k, max_seqlen_k, block_table, block_size,
+                                           max_blocks_per_seq, window_left, kv_dtype, k_scale,
+                                           v_scale, num_splits, workspace, workspace_bytes);
+    if (rc != GQA_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int rows = B * Hq;
+    float *ws_o = nullptr, *ws_lse = nullptr;
+    if (num_splits > 1) {
+        size_t o_bytes = (size_t)num_splits * rows * d * sizeof(float);
+        o_bytes = (o_bytes + 255) & ~size_t(255);
+        ws_o = static_cast<float *>(workspace);
+        ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
+    }
+    const bool fp8 = kv_dtype == GQA_DTYPE_FP8_E4M3;
+    gqa::DecodeParams p{};
+    p.q = q;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.o = out;
+    p.lse = lse;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Sk = max_seqlen_k;
+    p.G = Hq / Hkv;
+    p.n_qs = (p.G + 15) / 16;
+    p.num_splits = num_splits;
+    p.scale_log2 = scale * 1.4426950408889634f * (fp8 ? k_scale : 1.f);
+    p.v_scale = fp8 ? v_scale : 1.f;
+    p.seqlens = seqlens_k;
+    p.block_table = block_table;
+    p.log2_block = 0;
+    if (block_table)
+        while ((1 << p.log2_block) < block_size) ++p.log2_block;
+    p.max_blocks = max_blocks_per_seq;
+    p.window_left = window_left;
+    p.ws_o = ws_o;
+    p.ws_lse = ws_lse;
+    (void)hipGetLastError();
+    hipError_t e = gqa::launch_decode_bf16(p, d, block_table != nullptr, fp8, s);
+    if (e != hipSuccess || num_splits == 1) return status_from(e);
+    return status_from(
+        gqa::launch_decode_combine(ws_o, ws_lse, out, lse, rows, num_splits, d, true, s));
 }
 
 }  // extern "C"

@@ -22,6 +22,8 @@
 //    read as V^T with ds_read_b64_tr_b16. The next tile's loads are issued
 //    before the current tile's math.
 
+#include <type_traits>
+
 #include "device_util.h"
 #include "params.h"
 
@@ -37,7 +39,7 @@ template <int D>
 struct DecCfg {
     static constexpr int NS = D / 32;    // k-steps of 32 head_dim elements
     static constexpr int NDT = D / 16;   // 16-row tiles of O^T
-    static constexpr int NVL = D / 16;   // 16-byte V chunks per lane per tile
+    static constexpr int NVL = D / 16;   // 16-byte bf16 V chunks per lane per tile
     // V row stride in LDS (elements): the 32 lanes of a transposing read touch
     // rows r..r+3 and r+4..r+7; a stride of D + 16 puts their 8 segments of
     // 32 bytes on disjoint banks.
@@ -46,13 +48,30 @@ struct DecCfg {
     static constexpr int MERGE_BYTES = (NWAVES * D * 16 + 2 * NWAVES * 16) * 4;
     static constexpr int SMEM = VT_BYTES > MERGE_BYTES ? VT_BYTES : MERGE_BYTES;
 };
+// Block-table entries of one split kept in LDS (paged caches); a split with
+// more blocks reads the table from global memory instead.
+constexpr int MAX_TBL = 2048;
 
-template <int D>
-__global__ __launch_bounds__(NTHREADS) void decode_bf16_kernel(DecodeParams p) {
-    constexpr int NS = DecCfg<D>::NS, NDT = DecCfg<D>::NDT, NVL = DecCfg<D>::NVL;
+// fp8 e4m3 -> bf16 (exact) for 4 / 8 packed values.
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    const bf2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const bf2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
+template <int D, bool PAGED, bool FP8>
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2))) void
+decode_bf16_kernel(DecodeParams p) {
+    constexpr int NS = DecCfg<D>::NS, NDT = DecCfg<D>::NDT;
     constexpr int VRS = DecCfg<D>::VRS;
-    constexpr int C8 = D / 8;
+    constexpr int ESZ = FP8 ? 1 : 2;                // bytes per cached element
+    constexpr int VCH = 16 / ESZ;                   // elements per 16-byte V load
+    constexpr int VCPR = D / VCH;                   // V loads per row
+    constexpr int NVL = TK * VCPR / 64;             // V loads per lane per tile
+    typedef typename std::conditional<FP8, u32x2, bf16x8>::type kraw_t;  // K operand as loaded
     __shared__ __attribute__((aligned(16))) unsigned char smem[DecCfg<D>::SMEM];
+    __shared__ int tbl[PAGED ? MAX_TBL : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -71,8 +90,16 @@ __global__ __launch_bounds__(NTHREADS) void decode_bf16_kernel(DecodeParams p) {
     const bool q_ok = qg < p.G;
     const int head = kvh * p.G + qg;
 
-    const int k_lo = min(p.Sk, split * p.split_chunk);
-    const int k_hi = min(p.Sk, k_lo + p.split_chunk);
+    // This sequence's visible keys [vis_lo, L) (sliding window: the last
+    // window_left + 1 keys), cut into num_splits contiguous ranges of
+    // ceil(n / num_splits) keys rounded up to a multiple of 64.
+    const int L = p.seqlens ? min(max(p.seqlens[b], 0), p.Sk) : p.Sk;
+    const int vis_lo = p.window_left >= 0 ? max(0, L - 1 - p.window_left) : 0;
+    const int n = max(0, L - vis_lo);
+    int chunk = (n + p.num_splits - 1) / p.num_splits;
+    chunk = (chunk + 63) / 64 * 64;
+    const int k_lo = vis_lo + min(n, split * chunk);
+    const int k_hi = vis_lo + min(n, (split + 1) * chunk);
 
     // Q^T fragment (B operand): head_dim elements 32*s + 8*kq + j of query qi.
     bf16x8 qf[NS];
@@ -84,29 +111,60 @@ __global__ __launch_bounds__(NTHREADS) void decode_bf16_kernel(DecodeParams p) {
                          : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
 
-    const int64_t kv_stride = (int64_t)p.Hkv * D;
-    const __bf16 *kbase = (const __bf16 *)p.k + ((int64_t)b * p.Sk * p.Hkv + kvh) * D;
-    const __bf16 *vbase = (const __bf16 *)p.v + ((int64_t)b * p.Sk * p.Hkv + kvh) * D;
-    __bf16 *vsw = (__bf16 *)smem + wave * TK * VRS;  // this wave's V tile, row-major
+    // Paged cache: this split's block-table entries, staged in LDS.
+    int tbl_lo = 0;
+    bool tbl_lds = false;
+    if constexpr (PAGED) {
+        if (k_hi > k_lo) {
+            tbl_lo = k_lo >> p.log2_block;
+            const int nblk = ((k_hi - 1) >> p.log2_block) - tbl_lo + 1;
+            tbl_lds = nblk <= MAX_TBL;
+            if (tbl_lds)
+                for (int i = tid; i < nblk; i += NTHREADS)
+                    tbl[i] = p.block_table[(int64_t)b * p.max_blocks + tbl_lo + i];
+        }
+        __syncthreads();
+    }
+    // Element offset of key `key`'s row for K/V head kvh.
+    auto row_off = [&](int key) -> int64_t {
+        if constexpr (PAGED) {
+            const int blk = key >> p.log2_block;
+            const int page = tbl_lds ? tbl[blk - tbl_lo]
+                                     : p.block_table[(int64_t)b * p.max_blocks + blk];
+            const int64_t slot = ((int64_t)page << p.log2_block) | (key & ((1 << p.log2_block) - 1));
+            return (slot * p.Hkv + kvh) * D;
+        } else {
+            return ((int64_t)b * p.Sk + key) * p.Hkv * D + (int64_t)kvh * D;
+        }
+    };
+    const unsigned char *kbytes = (const unsigned char *)p.k;
+    const unsigned char *vbytes = (const unsigned char *)p.v;
+    __bf16 *vsw = (__bf16 *)smem + wave * TK * VRS;  // this wave's V tile, row-major bf16
 
-    bf16x8 kf[2][NS];
-    u32x4 vreg[NVL];
-    bf16x8 kf_n[2][NS];
-    u32x4 vreg_n[NVL];
+    kraw_t kf[2][NS], kf_n[2][NS];
+    u32x4 vreg[NVL], vreg_n[NVL];
 
-    auto load = [&](int t0, bf16x8 (&kd)[2][NS], u32x4 (&vd)[NVL]) {
+    auto load = [&](int t0, kraw_t (&kd)[2][NS], u32x4 (&vd)[NVL]) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             const int key = min(t0 + 16 * kt + qi, k_hi - 1);  // clamped; masked below
-            const __bf16 *krow = kbase + key * kv_stride + 8 * kq;
+            const unsigned char *krow = kbytes + (row_off(key) + 8 * kq) * ESZ;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) kd[kt][s] = *(const bf16x8 *)(krow + 32 * s);
+            for (int s = 0; s < NS; ++s) kd[kt][s] = *(const kraw_t *)(krow + 32 * s * ESZ);
         }
 #pragma unroll
         for (int i = 0; i < NVL; ++i) {  // whole rows: 16-byte chunk lane + 64 i
             const int c = lane + 64 * i;
-            const int key = min(t0 + c / C8, k_hi - 1);
-            vd[i] = *(const u32x4 *)(vbase + key * kv_stride + (c % C8) * 8);
+            const int key = min(t0 + c / VCPR, k_hi - 1);
+            vd[i] = *(const u32x4 *)(vbytes + (row_off(key) + (c % VCPR) * VCH) * ESZ);
+        }
+    };
+    auto k_operand = [&](const kraw_t &raw) -> bf16x8 {
+        if constexpr (FP8) {
+            const u32x2 lo = fp8x4_to_bf16x4(raw[0]), hi = fp8x4_to_bf16x4(raw[1]);
+            return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        } else {
+            return raw;
         }
     };
     // PV operand: in 16-lane group kq, lane j reads row 4 kq + j/4 (+16 for
@@ -123,11 +181,19 @@ __global__ __launch_bounds__(NTHREADS) void decode_bf16_kernel(DecodeParams p) {
     int t0 = k_lo + TK * wave;
     if (t0 < k_hi) load(t0, kf, vreg);
     for (; t0 < k_hi; t0 += TK * NWAVES) {
-        // V tile -> this wave's LDS slice, row-major.
+        // V tile -> this wave's LDS slice, row-major bf16.
 #pragma unroll
         for (int i = 0; i < NVL; ++i) {
-            const int c = lane + 64 * i;
-            *(u32x4 *)(vsw + (c / C8) * VRS + (c % C8) * 8) = vreg[i];
+            const int c8 = lane + 64 * i;
+            __bf16 *dst = vsw + (c8 / VCPR) * VRS + (c8 % VCPR) * VCH;
+            if constexpr (FP8) {
+                const u32x2 a = fp8x4_to_bf16x4(vreg[i][0]), b2 = fp8x4_to_bf16x4(vreg[i][1]);
+                const u32x2 c2 = fp8x4_to_bf16x4(vreg[i][2]), d2 = fp8x4_to_bf16x4(vreg[i][3]);
+                *(u32x4 *)dst = u32x4{a[0], a[1], b2[0], b2[1]};
+                *(u32x4 *)(dst + 8) = u32x4{c2[0], c2[1], d2[0], d2[1]};
+            } else {
+                *(u32x4 *)dst = vreg[i];
+            }
         }
         const int tn = t0 + TK * NWAVES;
         if (tn < k_hi) load(tn, kf_n, vreg_n);
@@ -139,7 +205,8 @@ __global__ __launch_bounds__(NTHREADS) void decode_bf16_kernel(DecodeParams p) {
             sacc[kt] = f32x4{};
 #pragma unroll
             for (int s = 0; s < NS; ++s)
-                sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kt][s], qf[s], sacc[kt], 0, 0, 0);
+                sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kf[kt][s]), qf[s], sacc[kt],
+                                                                   0, 0, 0);
         }
         if (t0 + TK > k_hi) {
 #pragma unroll
@@ -241,7 +308,7 @@ __global__ __launch_bounds__(NTHREADS) void decode_bf16_kernel(DecodeParams p) {
             }
         }
         const bool empty = !(l > 0.f);
-        const float val = empty ? 0.f : o / l;
+        const float val = empty ? 0.f : o / l * p.v_scale;
         const float lse = empty ? -INFINITY : (M + log2f(l)) * kLn2;
         const int64_t row = (int64_t)b * p.Hq + kvh * p.G + g2;
         if (p.num_splits == 1) {
@@ -294,16 +361,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeParams &p, int d, hipStream_t s) {
+hipError_t launch_decode_bf16(const DecodeParams &p, int d, bool paged, bool fp8_kv, hipStream_t s) {
     const long long grid = (long long)p.B * p.Hkv * p.num_splits * p.n_qs;
-    if (d == 64) {
-        hipLaunchKernelGGL(decode_bf16_kernel<64>, dim3((unsigned)grid), dim3(NTHREADS), 0, s, p);
-    } else if (d == 128) {
-        hipLaunchKernelGGL(decode_bf16_kernel<128>, dim3((unsigned)grid), dim3(NTHREADS), 0, s, p);
-    } else {
-        return hipErrorInvalidValue;
+#define GQA_CASE(D_, P_, F_)                                                                      \
+    if (d == D_ && paged == P_ && fp8_kv == F_) {                                                 \
+        hipLaunchKernelGGL((decode_bf16_kernel<D_, P_, F_>), dim3((unsigned)grid), dim3(NTHREADS), \
+                           0, s, p);                                                              \
+        return hipGetLastError();                                                                 \
     }
-    return hipGetLastError();
+    GQA_CASE(64, false, false)
+    GQA_CASE(64, true, false)
+    GQA_CASE(64, false, true)
+    GQA_CASE(64, true, true)
+    GQA_CASE(128, false, false)
+    GQA_CASE(128, true, false)
+    GQA_CASE(128, false, true)
+    GQA_CASE(128, true, true)
+#undef GQA_CASE
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_combine(const float *ws_o, const float *ws_lse, void *out, float *lse,

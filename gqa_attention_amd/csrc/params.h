@@ -31,25 +31,30 @@ struct FwdParams {
     float *ws_lse;
 };
 
-// One split-KV decode launch (bf16 kernel).
+// One split-KV decode launch (bf16 queries; bf16 or fp8 e4m3 K/V cache).
 struct DecodeParams {
     const void *q, *k, *v;
     void *o;
     float *lse;
-    int B, Hq, Hkv, Sk, G;
-    int n_qs;          // query slices of 16 heads per K/V head: ceil(G / 16)
+    int B, Hq, Hkv, Sk, G;       // Sk: keys per sequence, or the maximum when seqlens is set
+    int n_qs;                    // query slices of 16 heads per K/V head: ceil(G / 16)
     int num_splits;
-    int split_chunk;   // keys per split (multiple of 64)
-    float scale_log2;
-    float *ws_o;       // [num_splits, B*Hq, d] fp32, used when num_splits > 1
-    float *ws_lse;     // [num_splits, B*Hq] fp32
+    float scale_log2;            // scale * log2(e) (* k dequantisation scale for fp8)
+    float v_scale;               // V dequantisation scale (1 for bf16)
+    const int32_t *seqlens;      // [B] keys per sequence, or null (all Sk)
+    const int32_t *block_table;  // [B, max_blocks] page of each block of block_size keys, or null
+    int log2_block;              // log2(block_size) when paged
+    int max_blocks;
+    int window_left;             // -1: whole cache; W >= 0: keys j >= L - 1 - W
+    float *ws_o;                 // [num_splits, B*Hq, d] fp32, used when num_splits > 1
+    float *ws_lse;               // [num_splits, B*Hq] fp32
 };
 
 // Launchers (one per kernel family). Each returns a hipError_t.
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, bool causal, bool varlen, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams &p, int d, bool causal, bool varlen, bool split,
                           hipStream_t s);
-hipError_t launch_decode_bf16(const DecodeParams &p, int d, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeParams &p, int d, bool paged, bool fp8_kv, hipStream_t s);
 hipError_t launch_decode_combine(const float *ws_o, const float *ws_lse, void *out, float *lse,
                                  int rows, int num_splits, int d, bool out_bf16, hipStream_t s);
 

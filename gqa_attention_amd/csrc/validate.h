@@ -82,4 +82,37 @@ inline int validate_decode(const void *q, const void *kc, const void *vc, const 
     return GQA_OK;
 }
 
+inline bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+inline int validate_decode_ex(const void *q, const void *kc, const void *vc, const void *out,
+                              const float *lse, int B, int Hq, int Hkv, int d, float scale,
+                              const int32_t *seqlens, int max_seqlen_k, const int32_t *table,
+                              int block_size, int max_blocks, int window_left, int kv_dtype,
+                              float k_scale, float v_scale, int num_splits, const void *ws,
+                              size_t ws_bytes) {
+    if (!q || !kc || !vc || !out || !lse) return GQA_EINVAL;
+    if (kv_dtype != GQA_DTYPE_BF16 && kv_dtype != GQA_DTYPE_FP8_E4M3) return GQA_EUNSUPPORTED;
+    if (!supported_d(d)) return GQA_EUNSUPPORTED;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return GQA_EINVAL;
+    if (kv_dtype == GQA_DTYPE_FP8_E4M3 &&
+        (!std::isfinite(k_scale) || !(k_scale > 0.f) || !std::isfinite(v_scale) || !(v_scale > 0.f)))
+        return GQA_EINVAL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_seqlen_k < 1) return GQA_EINVAL;
+    if (window_left < -1) return GQA_EINVAL;
+    if (num_splits < 1 || num_splits > kMaxSplits) return GQA_EINVAL;
+    if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16) || !aligned(out, 16) ||
+        !aligned(lse, 4) || (seqlens && !aligned(seqlens, 4)))
+        return GQA_EINVAL;
+    if (table) {
+        if (!aligned(table, 4) || !is_pow2(block_size) || block_size > 4096) return GQA_EINVAL;
+        if ((long long)max_blocks * block_size < max_seqlen_k) return GQA_EINVAL;
+    }
+    if ((long long)B * Hkv * num_splits * ((Hq / Hkv + 15) / 16) > 0x7fffffffLL) return GQA_EINVAL;
+    if (num_splits > 1) {
+        if (!ws || !aligned(ws, 16)) return GQA_EWORKSPACE;
+        if (ws_bytes < decode_workspace_bytes(B, Hq, d, num_splits)) return GQA_EWORKSPACE;
+    }
+    return GQA_OK;
+}
+
 }  // namespace gqa

@@ -55,7 +55,8 @@ extern "C" {
 
 typedef enum {
     GQA_DTYPE_BF16 = 0,
-    GQA_DTYPE_FP32 = 1
+    GQA_DTYPE_FP32 = 1,
+    GQA_DTYPE_FP8_E4M3 = 2  /* K/V cache of gqa_attn_decode_ex only (OCP e4m3, 1 byte) */
 } gqa_dtype;
 
 enum {
@@ -116,6 +117,43 @@ int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache, voi
                     float *lse, int B, int Hq, int Hkv, int Sk, int d, float scale,
                     int num_splits, void *workspace, size_t workspace_bytes,
                     int dtype, void *stream);
+
+/*
+ * gqa_attn_decode_ex - decode over a ragged, optionally paged, optionally
+ * windowed, bf16 or fp8 K/V cache (the same split-KV method and LSE merge as
+ * gqa_attn_decode).
+ *
+ * Queries: q [B, Hq, d] bf16 -> out [B, Hq, d] bf16, lse [B, Hq] fp32.
+ * Cache, contiguous (block_table == NULL): k_cache, v_cache [B, max_seqlen_k, Hkv, d].
+ * Cache, paged (block_table != NULL, the fixed-size KV blocks named in the
+ *   Ultralytics glossary's PagedAttention item): k_cache, v_cache
+ *   [num_blocks, block_size, Hkv, d]; block_table int32 [B, max_blocks_per_seq]
+ *   on the device; key j of sequence b is slot j % block_size of block
+ *   block_table[b][j / block_size]. block_size must be a power of two
+ *   (1 .. 4096) and max_blocks_per_seq >= ceil(max_seqlen_k / block_size).
+ * seqlens_k: int32 [B] on the device (keys held by each sequence, 0 ..
+ *   max_seqlen_k; values outside that range are clamped into it), or NULL
+ *   when every sequence holds max_seqlen_k keys.
+ * window_left: -1 attends to every cached key; W >= 0 restricts each query to
+ *   the last W + 1 keys of its sequence (keys j >= L - 1 - W), the sliding
+ *   window of the glossary's related-techniques list.
+ * kv_dtype: GQA_DTYPE_BF16, or GQA_DTYPE_FP8_E4M3 with per-tensor
+ *   dequantisation scales (stored value x k_scale / v_scale; both ignored for
+ *   bf16). fp8 values are widened exactly to bf16 for the matrix cores.
+ * Splits: the visible keys of each sequence are cut into num_splits
+ *   contiguous ranges of ceil(n / num_splits) keys rounded up to a multiple of
+ *   64; workspace as for gqa_attn_decode. A sequence with no visible key gets
+ *   O = 0 and LSE = -inf.
+ * Errors: GQA_EINVAL for bad sizes, pointers, alignment, scales, block
+ * geometry or window; GQA_EUNSUPPORTED for d not in {64, 128} or an
+ * unsupported kv_dtype; GQA_EWORKSPACE as for gqa_attn_decode.
+ */
+int gqa_attn_decode_ex(const void *q, const void *k_cache, const void *v_cache, void *out,
+                       float *lse, int B, int Hq, int Hkv, int d, float scale,
+                       const int32_t *seqlens_k, int max_seqlen_k, const int32_t *block_table,
+                       int block_size, int max_blocks_per_seq, int window_left, int kv_dtype,
+                       float k_scale, float v_scale, int num_splits, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /* gqa_attn_strerror - static, NUL-terminated description of a status code. */
 const char *gqa_attn_strerror(int status);

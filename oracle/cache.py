@@ -51,13 +51,18 @@ def fp8_e4m3_decode(codes) -> np.ndarray:
 
 
 def stored_values(cache, fp8: bool, scale: float) -> np.ndarray:
-    """fp64 values a cache tensor stands for: bf16/fp32 exactly, fp8 as
-    decoded code x per-tensor scale."""
+    """fp64 values that stored cache elements stand for: bf16/fp32 exactly;
+    fp8 (a float8_e4m3fn tensor or its uint8 codes) as decoded code x the
+    per-tensor scale."""
     if not fp8:
         return _gqa.as_f64(cache)
     import torch
-    codes = cache.detach().cpu().contiguous().view(torch.uint8).numpy()
-    return fp8_e4m3_decode(codes) * float(scale)
+    if isinstance(cache, torch.Tensor):
+        if cache.dtype != torch.uint8:
+            cache = cache.contiguous().view(torch.uint8)
+        cache = cache.numpy()
+    table = fp8_e4m3_decode(np.arange(256))   # value of every code, looked up below
+    return table[np.asarray(cache, dtype=np.uint8)] * float(scale)
 
 
 def key_slots(b: int, n_keys: int, block_table: Optional[np.ndarray], block_size: int):
@@ -89,16 +94,19 @@ def decode_cache(q, k_cache, v_cache, scale: float, *, seqlens=None, block_table
     the contiguous cache's length). Returns O [B, Hq, d], LSE [B, Hq]; a
     sequence that sees no key gets O = 0, LSE = -inf.
     """
+    import torch
     qf = _gqa.as_f64(q)
-    kv = stored_values(k_cache, fp8, k_scale)
-    vv = stored_values(v_cache, fp8, v_scale)
+    # Gather each sequence's visible rows first (as raw storage: uint8 codes
+    # for fp8), then read their values.
+    kraw = k_cache.view(torch.uint8) if fp8 else k_cache
+    vraw = v_cache.view(torch.uint8) if fp8 else v_cache
     B, hq, d = qf.shape
     if block_table is None:
-        bs, cap = 0, kv.shape[1]
+        bs, cap = 0, kraw.shape[1]
         table = None
     else:
         table = np.asarray(_gqa.as_f64(block_table), dtype=np.int64)
-        bs = kv.shape[1]
+        bs = kraw.shape[1]
         cap = table.shape[1] * bs
     lens = [cap] * B if seqlens is None else [int(x) for x in np.asarray(_gqa.as_f64(seqlens))]
     out = np.zeros((B, hq, d))
@@ -107,8 +115,10 @@ def decode_cache(q, k_cache, v_cache, scale: float, *, seqlens=None, block_table
         L = lens[b]
         lo, hi = visible_range(L, window_left)
         page, slot = key_slots(b, L, table, bs)
-        keys = kv[page[lo:hi], slot[lo:hi]]      # [n, Hkv, d]
-        vals = vv[page[lo:hi], slot[lo:hi]]
+        pi = torch.as_tensor(page[lo:hi], dtype=torch.int64)
+        si = torch.as_tensor(slot[lo:hi], dtype=torch.int64)
+        keys = stored_values(kraw[pi, si], fp8, k_scale)      # [n, Hkv, d]
+        vals = stored_values(vraw[pi, si], fp8, v_scale)
         o, l = _gqa._sequence(qf[b][None], keys, vals, scale, False)
         out[b], lse[b] = o[0], l[:, 0]
     return out, lse

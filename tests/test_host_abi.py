@@ -30,8 +30,9 @@ def declared_functions():
 
 
 def test_header_declares_the_api():
-    assert declared_functions() == ["gqa_attn_decode", "gqa_attn_decode_workspace_bytes",
-                                    "gqa_attn_fwd", "gqa_attn_strerror"]
+    assert declared_functions() == ["gqa_attn_decode", "gqa_attn_decode_ex",
+                                    "gqa_attn_decode_workspace_bytes", "gqa_attn_fwd",
+                                    "gqa_attn_strerror"]
 
 
 @needs_lib
@@ -128,6 +129,57 @@ DEC_ERRORS = [
 @pytest.mark.parametrize("kw,code", DEC_ERRORS, ids=lambda x: str(x))
 def test_decode_argument_errors(kw, code):
     assert dec_call(**kw) == code
+
+
+def dex_call(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, B=2, Hq=8, Hkv=2, d=128, scale=0.1,
+             seqlens=FAKE, smax=100, table=FAKE, bs=16, nblk=7, window=-1, kv_dtype=0,
+             k_scale=1.0, v_scale=1.0, ns=4, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return ga.lib().gqa_attn_decode_ex(
+        a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["d"],
+        a["scale"], a["seqlens"], a["smax"], a["table"], a["bs"], a["nblk"], a["window"],
+        a["kv_dtype"], a["k_scale"], a["v_scale"], a["ns"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+DEX_ERRORS = [
+    (dict(q=None), ga.GQA_EINVAL),
+    (dict(lse=None), ga.GQA_EINVAL),
+    (dict(d=96), ga.GQA_EUNSUPPORTED),
+    (dict(kv_dtype=1), ga.GQA_EUNSUPPORTED),   # fp32 caches are not a decode_ex format
+    (dict(kv_dtype=3), ga.GQA_EUNSUPPORTED),
+    (dict(Hq=9), ga.GQA_EINVAL),
+    (dict(smax=0), ga.GQA_EINVAL),
+    (dict(window=-2), ga.GQA_EINVAL),
+    (dict(ns=0), ga.GQA_EINVAL),
+    (dict(ns=65), ga.GQA_EINVAL),
+    (dict(scale=float("nan")), ga.GQA_EINVAL),
+    (dict(kv_dtype=2, k_scale=0.0), ga.GQA_EINVAL),
+    (dict(kv_dtype=2, v_scale=float("inf")), ga.GQA_EINVAL),
+    (dict(bs=24), ga.GQA_EINVAL),              # page size not a power of two
+    (dict(bs=8192, nblk=1), ga.GQA_EINVAL),     # page size above 4096
+    (dict(bs=0), ga.GQA_EINVAL),
+    (dict(nblk=6), ga.GQA_EINVAL),             # 6 * 16 < max_seqlen_k 100
+    (dict(table=FAKE + 2), ga.GQA_EINVAL),
+    (dict(seqlens=FAKE + 2), ga.GQA_EINVAL),
+    (dict(v=FAKE + 8), ga.GQA_EINVAL),
+    (dict(ws=None), ga.GQA_EWORKSPACE),
+    (dict(ws_bytes=1000), ga.GQA_EWORKSPACE),
+]
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", DEX_ERRORS, ids=lambda x: str(x))
+def test_decode_ex_argument_errors(kw, code):
+    assert dex_call(**kw) == code
+
+
+@needs_lib
+def test_decode_ex_ignores_scales_and_page_size_when_unused():
+    # bf16 caches ignore the fp8 scales; a contiguous cache ignores the page geometry.
+    # Both calls still fail validation on a later, deliberate error (no launch).
+    assert dex_call(k_scale=0.0, v_scale=-1.0, ws=None) == ga.GQA_EWORKSPACE
+    assert dex_call(table=None, bs=24, nblk=0, ws=None) == ga.GQA_EWORKSPACE
 
 
 @needs_lib
