@@ -438,8 +438,12 @@ def main():
             del wd
         for cname in sorted(gqa_inputs.CACHE_NAMED):
             wc = gqa_inputs.CACHE_NAMED[cname]()
+            rec = ga.decode_num_splits(wc.batch, wc.q.shape[1], wc.k_cache.shape[2],
+                                       wc.q.shape[2], wc.max_seqlen_k, wc.window_left,
+                                       ragged=wc.seqlens is not None)
             for ns in (1, 2, 4, 8):
                 _, e = cache_entry(wc, ns, 20, 3)
+                e["recommended_num_splits"] = rec
                 extra.append(e)
             del wc
             torch.cuda.empty_cache()

@@ -15,7 +15,8 @@ Functions mirror the C entry points:
 * ``decode_ex(q, k_cache, v_cache, seqlens_k=None, block_table=None,
   window_left=-1, k_scale=1.0, v_scale=1.0, ...)`` -> ``(out, lse)``: decode
   over a ragged, paged, windowed, bf16 or fp8 e4m3 cache
-* ``decode_workspace_bytes(B, Hq, d, num_splits)``
+* ``decode_workspace_bytes(B, Hq, d, num_splits)``,
+  ``decode_num_splits(B, Hq, Hkv, d, max_seqlen_k, window_left=-1, ragged=False)``
 * ``FwdPlan`` / ``DecodePlan`` / ``DecodeExPlan``: the same calls marshalled
   once, re-issued by ``run()`` (for loops over fixed shapes and buffers)
 * ``strerror(status)``
@@ -30,7 +31,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["fwd", "decode", "decode_ex", "FwdPlan", "DecodePlan", "DecodeExPlan",
-           "decode_workspace_bytes", "strerror", "lib", "library_path",
+           "decode_workspace_bytes", "decode_num_splits", "strerror", "lib", "library_path",
            "GQA_OK", "GQA_EINVAL", "GQA_EUNSUPPORTED", "GQA_EWORKSPACE", "GQA_ELAUNCH",
            "GQA_DTYPE_BF16", "GQA_DTYPE_FP32", "GQA_DTYPE_FP8_E4M3", "GqaError"]
 
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.gqa_attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, i32, vp,
                                      i32, i32, i32, i32, f32, f32, i32, vp, sz, vp]
     L.gqa_attn_decode_ex.restype = i32
+    L.gqa_attn_decode_num_splits.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.gqa_attn_decode_num_splits.restype = i32
     L.gqa_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.gqa_attn_decode_workspace_bytes.restype = sz
     L.gqa_attn_strerror.argtypes = [i32]
@@ -219,6 +222,14 @@ class FwdPlan:
             if st:
                 _raise(st, "gqa_attn_fwd")
         return self.out, self.lse
+
+
+def decode_num_splits(B: int, Hq: int, Hkv: int, d: int, max_seqlen_k: int,
+                      window_left: int = -1, ragged: bool = False) -> int:
+    """Split count the library recommends for a decode of this shape (0 if
+    invalid); ``ragged``: the sequences' cache lengths differ."""
+    return int(lib().gqa_attn_decode_num_splits(B, Hq, Hkv, d, max_seqlen_k, window_left,
+                                                int(bool(ragged))))
 
 
 def decode_workspace_bytes(B: int, Hq: int, d: int, num_splits: int) -> int:

@@ -45,6 +45,11 @@ const char *gqa_attn_strerror(int status) {
     }
 }
 
+int gqa_attn_decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen_k, int window_left,
+                               int ragged) {
+    return gqa::decode_num_splits(B, Hq, Hkv, d, max_seqlen_k, window_left, ragged != 0);
+}
+
 size_t gqa_attn_decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
     return gqa::decode_workspace_bytes(B, Hq, d, num_splits);
 }

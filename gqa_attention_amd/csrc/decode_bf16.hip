@@ -31,6 +31,10 @@ namespace gqa {
 
 namespace {
 
+#ifndef GQA_DEC_WPE
+#define GQA_DEC_WPE 2  // waves per SIMD the register budget is sized for
+#endif
+
 constexpr int NTHREADS = 256;
 constexpr int NWAVES = 4;
 constexpr int TK = 32;        // keys per wave tile
@@ -48,9 +52,12 @@ struct DecCfg {
     static constexpr int MERGE_BYTES = (NWAVES * D * 16 + 2 * NWAVES * 16) * 4;
     static constexpr int SMEM = VT_BYTES > MERGE_BYTES ? VT_BYTES : MERGE_BYTES;
 };
-// Block-table entries of one split kept in LDS (paged caches); a split with
-// more blocks reads the table from global memory instead.
+// Block-table entries staged in LDS at a time (paged caches); a split that
+// spans more blocks is walked in windows of this many blocks.
 constexpr int MAX_TBL = 2048;
+// Ragged batches of at most this many sequences are scheduled longest first.
+constexpr int LPT_MAX = 256;
+static_assert(LPT_MAX <= NTHREADS, "one thread ranks one sequence");
 
 // fp8 e4m3 -> bf16 (exact) for 4 / 8 packed values.
 __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
@@ -61,7 +68,7 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
 }
 
 template <int D, bool PAGED, bool FP8>
-__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2))) void
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(GQA_DEC_WPE))) void
 decode_bf16_kernel(DecodeParams p) {
     constexpr int NS = DecCfg<D>::NS, NDT = DecCfg<D>::NDT;
     constexpr int VRS = DecCfg<D>::VRS;
@@ -77,29 +84,67 @@ decode_bf16_kernel(DecodeParams p) {
     const int lane = tid & 63, wave = tid >> 6;
     const int qi = lane & 15, kq = lane >> 4;
 
-    // blockIdx.x -> (query slice, split, K/V head, batch); slices fastest.
+    // blockIdx.x -> (query slice, split, K/V head, sequence rank); slices fastest.
     int id = blockIdx.x;
     const int qs = id % p.n_qs;
     id /= p.n_qs;
     const int split = id % p.num_splits;
     id /= p.num_splits;
     const int kvh = id % p.Hkv;
-    const int b = id / p.Hkv;
+    const int rank = id / p.Hkv;
 
     const int qg = qs * 16 + qi;  // head within the group
     const bool q_ok = qg < p.G;
     const int head = kvh * p.G + qg;
 
-    // This sequence's visible keys [vis_lo, L) (sliding window: the last
-    // window_left + 1 keys), cut into num_splits contiguous ranges of
+    // Keys of sequence x visible to its new token: [vis_lo, L), the last
+    // window_left + 1 keys with a sliding window.
+    auto seq_len = [&](int x) { return p.seqlens ? min(max(p.seqlens[x], 0), p.Sk) : p.Sk; };
+    auto first_visible = [&](int L) {
+        return p.window_left >= 0 ? max(0, L - 1 - p.window_left) : 0;
+    };
+
+    // Longest first: workgroups start roughly in blockIdx order, so with
+    // per-sequence lengths the sequence of rank r (r-th longest visible
+    // range, ties by index) gets the r-th group of workgroups. The biggest
+    // pieces start first and the short ones fill the tail.
+    int b = rank;
+    if (p.seqlens && p.B > 1 && p.B <= LPT_MAX) {
+        __shared__ int s_pick;
+        int *vis = (int *)smem;  // [B] visible lengths (smem holds V tiles later)
+        for (int x = tid; x < p.B; x += NTHREADS) {
+            const int Lx = seq_len(x);
+            vis[x] = Lx - first_visible(Lx);
+        }
+        __syncthreads();
+        if (tid < p.B) {
+            const int mine = vis[tid];
+            int r = 0;
+            for (int y = 0; y < p.B; ++y) {
+                const int o = vis[y];
+                r += (o > mine) || (o == mine && y < tid);
+            }
+            if (r == rank) s_pick = tid;
+        }
+        __syncthreads();
+        b = s_pick;
+    }
+
+    // This sequence's visible keys, cut into num_splits contiguous ranges of
     // ceil(n / num_splits) keys rounded up to a multiple of 64.
-    const int L = p.seqlens ? min(max(p.seqlens[b], 0), p.Sk) : p.Sk;
-    const int vis_lo = p.window_left >= 0 ? max(0, L - 1 - p.window_left) : 0;
-    const int n = max(0, L - vis_lo);
-    int chunk = (n + p.num_splits - 1) / p.num_splits;
-    chunk = (chunk + 63) / 64 * 64;
-    const int k_lo = vis_lo + min(n, split * chunk);
-    const int k_hi = vis_lo + min(n, (split + 1) * chunk);
+    const int L = seq_len(b);
+    const int vis_lo = first_visible(L);
+    const int n = L - vis_lo;
+    const int chunk = (int)((((int64_t)n + p.num_splits - 1) / p.num_splits + 63) & ~(int64_t)63);
+    const int k_lo = vis_lo + (int)min((int64_t)n, (int64_t)split * chunk);
+    const int k_hi = vis_lo + (int)min((int64_t)n, (int64_t)(split + 1) * chunk);
+    const int rows = p.B * p.Hq;
+    if (p.num_splits > 1 && k_hi <= k_lo) {
+        // A split past the sequence's end: the merge only needs its LSE (-inf).
+        if (tid < 16 && qs * 16 + tid < p.G)
+            p.ws_lse[(int64_t)split * rows + (int64_t)b * p.Hq + kvh * p.G + qs * 16 + tid] = -INFINITY;
+        return;
+    }
 
     // Q^T fragment (B operand): head_dim elements 32*s + 8*kq + j of query qi.
     bf16x8 qf[NS];
@@ -111,52 +156,45 @@ decode_bf16_kernel(DecodeParams p) {
                          : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
 
-    // Paged cache: this split's block-table entries, staged in LDS.
+    // Byte addressing. Consecutive keys of one K/V head are row_bytes apart
+    // (contiguous cache: [B, Sk, Hkv, D]; paged: [pages, block, Hkv, D]).
+    // Lane bases fold in the head and the lane's fixed column.
+    const int64_t row_bytes = (int64_t)p.Hkv * D * ESZ;
+    const int64_t head_off = (int64_t)kvh * D * ESZ + (PAGED ? 0 : (int64_t)b * p.Sk * row_bytes);
+    const unsigned char *kbase = (const unsigned char *)p.k + head_off + 8 * kq * ESZ;
+    const unsigned char *vbase = (const unsigned char *)p.v + head_off + (lane % VCPR) * 16;
+    const int lb = PAGED ? p.log2_block : 0;
+    const int64_t page_bytes = row_bytes << lb;
+    const int slot_mask = (1 << lb) - 1;
     int tbl_lo = 0;
-    bool tbl_lds = false;
-    if constexpr (PAGED) {
-        if (k_hi > k_lo) {
-            tbl_lo = k_lo >> p.log2_block;
-            const int nblk = ((k_hi - 1) >> p.log2_block) - tbl_lo + 1;
-            tbl_lds = nblk <= MAX_TBL;
-            if (tbl_lds)
-                for (int i = tid; i < nblk; i += NTHREADS)
-                    tbl[i] = p.block_table[(int64_t)b * p.max_blocks + tbl_lo + i];
-        }
-        __syncthreads();
-    }
-    // Element offset of key `key`'s row for K/V head kvh.
-    auto row_off = [&](int key) -> int64_t {
+    // Address of key `key` (which must lie in the staged table window when paged).
+    auto key_ptr = [&](const unsigned char *base, int key) -> const unsigned char * {
         if constexpr (PAGED) {
-            const int blk = key >> p.log2_block;
-            const int page = tbl_lds ? tbl[blk - tbl_lo]
-                                     : p.block_table[(int64_t)b * p.max_blocks + blk];
-            const int64_t slot = ((int64_t)page << p.log2_block) | (key & ((1 << p.log2_block) - 1));
-            return (slot * p.Hkv + kvh) * D;
+            const int page = tbl[(key >> lb) - tbl_lo];
+            return base + page * page_bytes + (int64_t)(key & slot_mask) * row_bytes;
         } else {
-            return ((int64_t)b * p.Sk + key) * p.Hkv * D + (int64_t)kvh * D;
+            return base + (int64_t)key * row_bytes;
         }
     };
-    const unsigned char *kbytes = (const unsigned char *)p.k;
-    const unsigned char *vbytes = (const unsigned char *)p.v;
     __bf16 *vsw = (__bf16 *)smem + wave * TK * VRS;  // this wave's V tile, row-major bf16
 
     kraw_t kf[2][NS], kf_n[2][NS];
     u32x4 vreg[NVL], vreg_n[NVL];
+    int w_hi = k_hi;  // end of the current table window
 
+    // Tile t0's K rows (keys t0 + 16 kt + qi) and V rows (16-byte chunk lane + 64 i
+    // of the tile), clamped into [k_lo, w_hi); clamped rows are masked below.
     auto load = [&](int t0, kraw_t (&kd)[2][NS], u32x4 (&vd)[NVL]) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-            const int key = min(t0 + 16 * kt + qi, k_hi - 1);  // clamped; masked below
-            const unsigned char *krow = kbytes + (row_off(key) + 8 * kq) * ESZ;
+            const unsigned char *krow = key_ptr(kbase, min(t0 + 16 * kt + qi, w_hi - 1));
 #pragma unroll
             for (int s = 0; s < NS; ++s) kd[kt][s] = *(const kraw_t *)(krow + 32 * s * ESZ);
         }
 #pragma unroll
-        for (int i = 0; i < NVL; ++i) {  // whole rows: 16-byte chunk lane + 64 i
-            const int c = lane + 64 * i;
-            const int key = min(t0 + c / VCPR, k_hi - 1);
-            vd[i] = *(const u32x4 *)(vbytes + (row_off(key) + (c % VCPR) * VCH) * ESZ);
+        for (int i = 0; i < NVL; ++i) {
+            const int key = min(t0 + lane / VCPR + i * (64 / VCPR), w_hi - 1);
+            vd[i] = *(const u32x4 *)key_ptr(vbase, key);
         }
     };
     auto k_operand = [&](const kraw_t &raw) -> bf16x8 {
@@ -178,96 +216,111 @@ decode_bf16_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < NDT; ++i) oacc[i] = f32x4{};
 
-    int t0 = k_lo + TK * wave;
-    if (t0 < k_hi) load(t0, kf, vreg);
-    for (; t0 < k_hi; t0 += TK * NWAVES) {
-        // V tile -> this wave's LDS slice, row-major bf16.
+    // Paged caches stage the block-table entries of a window of at most
+    // MAX_TBL blocks in LDS and walk the split window by window (one window
+    // unless the split spans more than MAX_TBL blocks); contiguous caches
+    // have a single window.
+    for (int w_lo = k_lo; w_lo < k_hi; w_lo = w_hi) {
+        if constexpr (PAGED) {
+            tbl_lo = w_lo >> lb;
+            w_hi = (int)min((int64_t)k_hi, ((int64_t)tbl_lo + MAX_TBL) << lb);
+            const int nblk = ((w_hi - 1) >> lb) - tbl_lo + 1;
+            __syncthreads();  // every wave is done with the previous window's entries
+            for (int i = tid; i < nblk; i += NTHREADS)
+                tbl[i] = p.block_table[(int64_t)b * p.max_blocks + tbl_lo + i];
+            __syncthreads();
+        }
+        int t0 = w_lo + TK * wave;
+        if (t0 < w_hi) load(t0, kf, vreg);
+        for (; t0 < w_hi; t0 += TK * NWAVES) {
+            // V tile -> this wave's LDS slice, row-major bf16.
 #pragma unroll
-        for (int i = 0; i < NVL; ++i) {
-            const int c8 = lane + 64 * i;
-            __bf16 *dst = vsw + (c8 / VCPR) * VRS + (c8 % VCPR) * VCH;
-            if constexpr (FP8) {
-                const u32x2 a = fp8x4_to_bf16x4(vreg[i][0]), b2 = fp8x4_to_bf16x4(vreg[i][1]);
-                const u32x2 c2 = fp8x4_to_bf16x4(vreg[i][2]), d2 = fp8x4_to_bf16x4(vreg[i][3]);
-                *(u32x4 *)dst = u32x4{a[0], a[1], b2[0], b2[1]};
-                *(u32x4 *)(dst + 8) = u32x4{c2[0], c2[1], d2[0], d2[1]};
-            } else {
-                *(u32x4 *)dst = vreg[i];
+            for (int i = 0; i < NVL; ++i) {
+                const int c8 = lane + 64 * i;
+                __bf16 *dst = vsw + (c8 / VCPR) * VRS + (c8 % VCPR) * VCH;
+                if constexpr (FP8) {
+                    const u32x2 a = fp8x4_to_bf16x4(vreg[i][0]), b2 = fp8x4_to_bf16x4(vreg[i][1]);
+                    const u32x2 c2 = fp8x4_to_bf16x4(vreg[i][2]), d2 = fp8x4_to_bf16x4(vreg[i][3]);
+                    *(u32x4 *)dst = u32x4{a[0], a[1], b2[0], b2[1]};
+                    *(u32x4 *)(dst + 8) = u32x4{c2[0], c2[1], d2[0], d2[1]};
+                } else {
+                    *(u32x4 *)dst = vreg[i];
+                }
             }
-        }
-        const int tn = t0 + TK * NWAVES;
-        if (tn < k_hi) load(tn, kf_n, vreg_n);
+            const int tn = t0 + TK * NWAVES;
+            if (tn < w_hi) load(tn, kf_n, vreg_n);
 
-        // S^T = K Q^T: 2 tiles of 16 keys x 16 query heads.
-        f32x4 sacc[2];
+            // S^T = K Q^T: 2 tiles of 16 keys x 16 query heads.
+            f32x4 sacc[2];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            sacc[kt] = f32x4{};
+            for (int kt = 0; kt < 2; ++kt) {
+                sacc[kt] = f32x4{};
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
-                sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kf[kt][s]), qf[s], sacc[kt],
-                                                                   0, 0, 0);
-        }
-        if (t0 + TK > k_hi) {
+                for (int s = 0; s < NS; ++s)
+                    sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kf[kt][s]), qf[s],
+                                                                       sacc[kt], 0, 0, 0);
+            }
+            if (t0 + TK > w_hi) {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (t0 + 16 * kt + 4 * kq + r >= w_hi) sacc[kt][r] = -INFINITY;
+            }
+            float mx = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (t0 + 16 * kt + 4 * kq + r >= k_hi) sacc[kt][r] = -INFINITY;
-        }
-        float mx = -INFINITY;
+                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kt][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = pair_max32(mx);
+            // Move the reference max only when it is exceeded by more than
+            // kRescaleGap (see fwd_bf16.hip); the result is unchanged.
+            const float mxs = mx * c;
+            if (mxs > m_run + kRescaleGap) {
+                const float alpha = fast_exp2(m_run - mxs);
+                m_run = mxs;
+                l_run *= alpha;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+                for (int i = 0; i < NDT; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = pair_max32(mx);
-        // Move the reference max only when it is exceeded by more than
-        // kRescaleGap (see fwd_bf16.hip); the result is unchanged.
-        const float mxs = mx * c;
-        if (mxs > m_run + kRescaleGap) {
-            const float alpha = fast_exp2(m_run - mxs);
-            m_run = mxs;
-            l_run *= alpha;
-#pragma unroll
-            for (int i = 0; i < NDT; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) oacc[i][r] *= alpha;
-        }
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        bf16x8 pf;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float pv = fast_exp2(fmaf(sacc[kt][r], c, -m_use));
-                l_run += pv;
-                pf[4 * kt + r] = (__bf16)pv;
+                    for (int r = 0; r < 4; ++r) oacc[i][r] *= alpha;
             }
-
-        // O^T += V^T P^T; k-slot j of lane (qi, kq) is key 16*(j/4) + 4*kq + j%4.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int i = 0; i < NDT; ++i) {
-            const __bf16 *vp = vsw + 16 * i + v_rd;
-            const u32x2 lo = lds_read_tr16(vp);
-            const u32x2 hi = lds_read_tr16(vp + 16 * VRS);
-            const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-            oacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, oacc[i], 0, 0, 0);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        if (tn < k_hi) {
+            const float m_use = m_run == -INFINITY ? 0.f : m_run;
+            bf16x8 pf;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int s = 0; s < NS; ++s) kf[kt][s] = kf_n[kt][s];
+                for (int r = 0; r < 4; ++r) {
+                    const float pv = fast_exp2(fmaf(sacc[kt][r], c, -m_use));
+                    l_run += pv;
+                    pf[4 * kt + r] = (__bf16)pv;
+                }
+
+            // O^T += V^T P^T; k-slot j of lane (qi, kq) is key 16*(j/4) + 4*kq + j%4.
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-            for (int i = 0; i < NVL; ++i) vreg[i] = vreg_n[i];
+            for (int i = 0; i < NDT; ++i) {
+                const __bf16 *vp = vsw + 16 * i + v_rd;
+                const u32x2 lo = lds_read_tr16(vp);
+                const u32x2 hi = lds_read_tr16(vp + 16 * VRS);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                oacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, oacc[i], 0, 0, 0);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+            if (tn < w_hi) {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) kf[kt][s] = kf_n[kt][s];
+#pragma unroll
+                for (int i = 0; i < NVL; ++i) vreg[i] = vreg_n[i];
+            }
         }
     }
 
@@ -290,7 +343,6 @@ decode_bf16_kernel(DecodeParams p) {
     }
     __syncthreads();
 
-    const int rows = p.B * p.Hq;
     for (int idx = tid; idx < 16 * D; idx += NTHREADS) {
         const int q2 = idx / D, d = idx - q2 * D;
         const int g2 = qs * 16 + q2;
@@ -339,7 +391,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     float tot = 0.f;
     if (M != -INFINITY) {
         for (int s = 0; s < ns; ++s) {
-            const float w = __expf(ws_lse[(int64_t)s * rows + row] - M);
+            const float ls = ws_lse[(int64_t)s * rows + row];
+            if (ls == -INFINITY) continue;  // empty split: its O_s is not written
+            const float w = __expf(ls - M);
             tot += w;
             const float *src = ws_o + ((int64_t)s * rows + row) * D;
 #pragma unroll

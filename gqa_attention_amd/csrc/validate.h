@@ -59,8 +59,9 @@ inline size_t decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
 }
 
 inline int split_chunk(int Sk, int num_splits) {
-    int chunk = (Sk + num_splits - 1) / num_splits;
-    return (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+    const long long chunk = ((long long)Sk + num_splits - 1) / num_splits;
+    const long long aligned_chunk = (chunk + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+    return (int)(aligned_chunk < 0x7fffffc0LL ? aligned_chunk : 0x7fffffc0LL);
 }
 
 inline int validate_decode(const void *q, const void *kc, const void *vc, const void *out,
@@ -113,6 +114,24 @@ inline int validate_decode_ex(const void *q, const void *kc, const void *vc, con
         if (ws_bytes < decode_workspace_bytes(B, Hq, d, num_splits)) return GQA_EWORKSPACE;
     }
     return GQA_OK;
+}
+
+// Split count for decode (measured on MI355X): enough splits that the launch
+// has about 192 or more workgroups (at least 2 for ragged batches), but at
+// least 512 keys per split.
+inline int decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen_k, int window_left,
+                             bool ragged) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || !supported_d(d) || max_seqlen_k < 1 ||
+        window_left < -1)
+        return 0;
+    const long long units = (long long)B * Hkv * ((Hq / Hkv + 15) / 16);
+    int ns = units >= 192 ? 1 : units >= 96 ? 2 : units >= 48 ? 4 : units >= 12 ? 8 : 16;
+    if (ragged && ns < 2) ns = 2;
+    const long long keys = window_left >= 0 && (long long)window_left + 1 < max_seqlen_k
+                               ? (long long)window_left + 1
+                               : max_seqlen_k;
+    while (ns > 1 && keys / ns < 512) ns >>= 1;
+    return ns;
 }
 
 }  // namespace gqa

@@ -141,9 +141,10 @@ int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache, voi
  *   dequantisation scales (stored value x k_scale / v_scale; both ignored for
  *   bf16). fp8 values are widened exactly to bf16 for the matrix cores.
  * Splits: the visible keys of each sequence are cut into num_splits
- *   contiguous ranges of ceil(n / num_splits) keys rounded up to a multiple of
- *   64; workspace as for gqa_attn_decode. A sequence with no visible key gets
- *   O = 0 and LSE = -inf.
+ *   contiguous ranges of ceil(n / num_splits) keys rounded up to a multiple
+ *   of 64 (trailing ranges may be empty); workspace as for gqa_attn_decode.
+ *   With seqlens_k and B <= 256 the workgroups take the sequences longest
+ *   first. A sequence with no visible key gets O = 0 and LSE = -inf.
  * Errors: GQA_EINVAL for bad sizes, pointers, alignment, scales, block
  * geometry or window; GQA_EUNSUPPORTED for d not in {64, 128} or an
  * unsupported kv_dtype; GQA_EWORKSPACE as for gqa_attn_decode.
@@ -154,6 +155,25 @@ int gqa_attn_decode_ex(const void *q, const void *k_cache, const void *v_cache, 
                        int block_size, int max_blocks_per_seq, int window_left, int kv_dtype,
                        float k_scale, float v_scale, int num_splits, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/*
+ * gqa_attn_decode_num_splits - a split count for gqa_attn_decode /
+ * gqa_attn_decode_ex on MI355X (the gitcode GQA guide's num_splits knob; its
+ * A100/H100 table is prior art for other chips and is not used).
+ *
+ * Measured rule: a decode launch has B * Hkv * ceil(G / 16) workgroups per
+ * split; splits are added until there are about 192 or more of them
+ * (units >= 192 -> 1, >= 96 -> 2, >= 48 -> 4, >= 12 -> 8, else 16). A ragged
+ * batch (ragged != 0: per-sequence lengths that differ) takes at least 2, so
+ * that its longest sequences are cut and scheduled first. The count is then
+ * halved while a split would get fewer than 512 keys of the longest visible
+ * range (max_seqlen_k, or window_left + 1 when smaller). On the split-count
+ * sweep of bf16 caches (B 1..128, 512..32768 keys, d 64 and 128) this choice
+ * is within 17% of the best count and usually within a few percent.
+ * Returns 0 for invalid arguments (same rules as gqa_attn_decode_ex).
+ */
+int gqa_attn_decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen_k, int window_left,
+                               int ragged);
 
 /* gqa_attn_strerror - static, NUL-terminated description of a status code. */
 const char *gqa_attn_strerror(int status);

@@ -1,10 +1,11 @@
 """GPU parity of decode over a general K/V cache (``gqa_attn_decode_ex``)
 against the fp64 oracle ``oracle.cache.decode_cache`` on seeded inputs.
 
-Covers contiguous and paged caches (page sizes 1 to 256, a split whose block
-table is too long to stage and is read from global memory), per-sequence
+Covers contiguous and paged caches (page sizes 1 to 256, a split spanning
+more blocks than one staged window of the block table), per-sequence
 lengths with empty and one-key caches and lengths around the 64-key split
-granularity, sliding windows (one key, narrower and wider than the cache),
+granularity, ragged batches of up to 256 sequences (scheduled longest first)
+and of more, sliding windows (one key, narrower and wider than the cache),
 fp8 e4m3 storage with dequantisation scales, MHA / GQA / MQA head ratios
 including groups of 16 and 24 query heads, and several split counts; plus
 exact identities: the contiguous full-length call equals ``gqa_attn_decode``
@@ -64,6 +65,8 @@ CASES = [
     ([0, 1, 63, 300, 1000], 32, 8, 128, 16, -1, True, 3),
     ([129, 2000], 8, 2, 64, 32, 511, True, 2),
     ([333], 24, 3, 64, 8, -1, True, 1),                   # group of 8
+    ([(37 * i) % 211 for i in range(300)], 8, 2, 64, 16, -1, False, 2),  # no longest-first
+    ([(53 * i) % 997 for i in range(256)], 8, 2, 64, 0, -1, False, 3),   # longest-first, 256
 ]
 
 

@@ -31,6 +31,7 @@ def declared_functions():
 
 def test_header_declares_the_api():
     assert declared_functions() == ["gqa_attn_decode", "gqa_attn_decode_ex",
+                                    "gqa_attn_decode_num_splits",
                                     "gqa_attn_decode_workspace_bytes", "gqa_attn_fwd",
                                     "gqa_attn_strerror"]
 
@@ -202,3 +203,24 @@ def test_python_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
     with pytest.raises((ValueError, RuntimeError)):
         ga.fwd(q, q[:, :, :1].contiguous(), q[:, :, :1].contiguous())
+
+
+@needs_lib
+def test_decode_num_splits_rule():
+    f = ga.decode_num_splits
+    # Llama 3.1 8B heads (32 / 8, one 16-head slice per K/V head)
+    assert f(64, 32, 8, 128, 4096) == 1          # 512 workgroups already
+    assert f(16, 32, 8, 128, 8192) == 2          # 128 -> 2 splits
+    assert f(8, 32, 8, 128, 8192) == 4           # 64 -> 4
+    assert f(4, 32, 8, 128, 32768) == 8          # 32 -> 8
+    assert f(1, 32, 8, 128, 32768) == 16         # 8 -> 16
+    assert f(1, 32, 8, 128, 2048) == 4           # capped: at least 512 keys per split
+    assert f(1, 32, 8, 128, 512) == 1
+    assert f(1, 32, 8, 128, 100000, 1023) == 2   # a 1024-key window bounds the range
+    assert f(1, 48, 1, 64, 32768) == 16          # 48 heads on one K/V head: 3 slices
+    assert f(4, 48, 1, 64, 32768) == 8
+    assert f(64, 32, 8, 128, 8192, ragged=True) == 2   # ragged: at least 2 splits
+    assert f(64, 32, 8, 128, 800, ragged=True) == 1    # ... unless splits get < 512 keys
+    for bad in [(0, 32, 8, 128, 10), (1, 30, 8, 128, 10), (1, 32, 8, 96, 10),
+                (1, 32, 8, 128, 0), (1, 32, 8, 128, 10, -2)]:
+        assert f(*bad) == 0, bad
