@@ -10,9 +10,11 @@ Modules:
   kv_cache   KV-cache size arithmetic pinned to the glossary's printed figures
   cache      decode over a general cache: per-sequence lengths, pages, a
              sliding window, fp8 (e4m3) storage
+  backward   gradients dq, dk, dv of the definition (chain rule, materialised)
 """
 from .gqa import (attention, attention_rows, decode, decode_partials,  # noqa: F401
                         merge_partials, split_ranges, attention_flops, head_rows,
                         expand_kv, kv_head_of, visible, as_f64)
 from .kv_cache import kv_cache_bytes, kv_cache_elements  # noqa: F401
 from .cache import decode_cache, fp8_e4m3_decode  # noqa: F401
+from .backward import attention_grad, attention_grad_flops  # noqa: F401
