@@ -12,13 +12,16 @@ Functions mirror the C entry points:
   max_seqlen_q=None, max_seqlen_k=None)`` -> ``(out, lse)``
 * ``decode(q, k_cache, v_cache, scale=None, num_splits=1, workspace=None)`` ->
   ``(out, lse)``
+* ``bwd(q, k, v, out, lse, dout, causal=False, scale=None, cu_seqlens_q=None,
+  cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None)`` -> ``(dq, dk, dv)``
 * ``decode_ex(q, k_cache, v_cache, seqlens_k=None, block_table=None,
   window_left=-1, k_scale=1.0, v_scale=1.0, ...)`` -> ``(out, lse)``: decode
   over a ragged, paged, windowed, bf16 or fp8 e4m3 cache
 * ``decode_workspace_bytes(B, Hq, d, num_splits)``,
   ``decode_num_splits(B, Hq, Hkv, d, max_seqlen_k, window_left=-1, ragged=False)``
-* ``FwdPlan`` / ``DecodePlan`` / ``DecodeExPlan``: the same calls marshalled
-  once, re-issued by ``run()`` (for loops over fixed shapes and buffers)
+* ``FwdPlan`` / ``BwdPlan`` / ``DecodePlan`` / ``DecodeExPlan``: the same
+  calls marshalled once, re-issued by ``run()`` (for loops over fixed shapes
+  and buffers)
 * ``strerror(status)``
 """
 from __future__ import annotations
@@ -30,7 +33,8 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["fwd", "decode", "decode_ex", "FwdPlan", "DecodePlan", "DecodeExPlan",
+__all__ = ["fwd", "bwd", "decode", "decode_ex", "FwdPlan", "BwdPlan", "DecodePlan", "DecodeExPlan",
+           "bwd_workspace_bytes",
            "decode_workspace_bytes", "decode_num_splits", "strerror", "lib", "library_path",
            "GQA_OK", "GQA_EINVAL", "GQA_EUNSUPPORTED", "GQA_EWORKSPACE", "GQA_ELAUNCH",
            "GQA_DTYPE_BF16", "GQA_DTYPE_FP32", "GQA_DTYPE_FP8_E4M3", "GqaError"]
@@ -75,6 +79,11 @@ def lib() -> ctypes.CDLL:
     L.gqa_attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, i32, vp,
                                      i32, i32, i32, i32, f32, f32, i32, vp, sz, vp]
     L.gqa_attn_decode_ex.restype = i32
+    L.gqa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                               f32, i32, vp, vp, vp, sz, i32, vp]
+    L.gqa_attn_bwd.restype = i32
+    L.gqa_attn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.gqa_attn_bwd_workspace_bytes.restype = sz
     L.gqa_attn_decode_num_splits.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.gqa_attn_decode_num_splits.restype = i32
     L.gqa_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -222,6 +231,80 @@ class FwdPlan:
             if st:
                 _raise(st, "gqa_attn_fwd")
         return self.out, self.lse
+
+
+def bwd_workspace_bytes(B: int, Hq: int, Hkv: int, Sq: int) -> int:
+    return int(lib().gqa_attn_bwd_workspace_bytes(B, Hq, Hkv, Sq))
+
+
+def _prepare_bwd(q, k, v, out, lse, dout, causal, scale, cu_seqlens_q, cu_seqlens_k,
+                 max_seqlen_q, max_seqlen_k, dq, dk, dv, workspace):
+    """Check metadata, allocate gradients and workspace, build the C arguments."""
+    _, _, fargs, empty = _prepare_fwd(q, k, v, causal, scale, cu_seqlens_q, cu_seqlens_k,
+                                      max_seqlen_q, max_seqlen_k, out, lse)
+    dev = q.device
+    _check("dout", dout, q.dim(), q.dtype, dev)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    if q.dtype != torch.bfloat16:
+        raise ValueError("the backward supports bfloat16 inputs")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check(name, t, ref.dim(), ref.dtype, dev)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} must have shape {tuple(ref.shape)}")
+    (qp, kp, vp_, op, lp, B, Hq, Hkv, Sq, Sk, d, sc, causal_i, cq, ck, code) = fargs
+    need = bwd_workspace_bytes(B, Hq, Hkv, Sq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args = (qp, kp, vp_, op, lp, dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+            B, Hq, Hkv, Sq, Sk, d, sc, causal_i, cq, ck, workspace.data_ptr(), ws_bytes, code)
+    return dq, dk, dv, workspace, args
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+        dout: torch.Tensor, *, causal: bool = False, scale: Optional[float] = None,
+        cu_seqlens_q: Optional[torch.Tensor] = None, cu_seqlens_k: Optional[torch.Tensor] = None,
+        max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+        dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+        dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+        ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Gradients of ``fwd`` through ``gqa_attn_bwd`` (bf16).
+
+    ``out`` and ``lse`` are ``fwd``'s results for the same inputs and
+    arguments; ``dout`` is the gradient of ``out``. Returns (dq, dk, dv) in
+    the layouts of q, k, v.
+    """
+    dq, dk, dv, _, args = _prepare_bwd(q, k, v, out, lse, dout, causal, scale, cu_seqlens_q,
+                                       cu_seqlens_k, max_seqlen_q, max_seqlen_k, dq, dk, dv,
+                                       workspace)
+    with torch.cuda.device(q.device):
+        st = lib().gqa_attn_bwd(*args, _stream_handle(q.device))
+    _raise(st, "gqa_attn_bwd")
+    return dq, dk, dv
+
+
+class BwdPlan:
+    """A backward call checked and marshalled once; ``run()`` re-issues it."""
+
+    def __init__(self, q, k, v, out, lse, dout, *, causal=False, scale=None, cu_seqlens_q=None,
+                 cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, dq=None, dk=None,
+                 dv=None, workspace=None):
+        self.dq, self.dk, self.dv, self.workspace, self._args = _prepare_bwd(
+            q, k, v, out, lse, dout, causal, scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+            max_seqlen_k, dq, dk, dv, workspace)
+        self._keep = (q, k, v, out, lse, dout, cu_seqlens_q, cu_seqlens_k)
+        self._dev = q.device
+        self._fn = lib().gqa_attn_bwd
+
+    def run(self):
+        st = self._fn(*self._args, _stream_handle(self._dev))
+        if st:
+            _raise(st, "gqa_attn_bwd")
+        return self.dq, self.dk, self.dv
 
 
 def decode_num_splits(B: int, Hq: int, Hkv: int, d: int, max_seqlen_k: int,

@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libgqa_attn.so")
 PROBE = os.path.join(PKG, "hbm_probe")  # copy / read-stream reference program
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode_bf16.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode_bf16.hip", "bwd_bf16.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

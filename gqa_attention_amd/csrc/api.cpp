@@ -14,6 +14,7 @@
 namespace gqa {
 int fwd_bf16_rows_per_tile();
 int fwd_f32_rows_per_tile();
+int bwd_rows_per_tile();
 }  // namespace gqa
 
 namespace {
@@ -48,6 +49,51 @@ const char *gqa_attn_strerror(int status) {
 int gqa_attn_decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen_k, int window_left,
                                int ragged) {
     return gqa::decode_num_splits(B, Hq, Hkv, d, max_seqlen_k, window_left, ragged != 0);
+}
+
+size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq) {
+    return gqa::bwd_workspace_bytes(B, Hq, Hkv, Sq);
+}
+
+int gqa_attn_bwd(const void *q, const void *k, const void *v, const void *out, const float *lse,
+                 const void *dout, void *dq, void *dk, void *dv, int B, int Hq, int Hkv, int Sq,
+                 int Sk, int d, float scale, int causal, const int32_t *cu_seqlens_q,
+                 const int32_t *cu_seqlens_k, void *workspace, size_t workspace_bytes, int dtype,
+                 void *stream) {
+    const int rc = gqa::validate_bwd(q, k, v, out, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Sk, d,
+                                     scale, cu_seqlens_q, cu_seqlens_k, workspace,
+                                     workspace_bytes, dtype);
+    if (rc != GQA_OK) return rc;
+    gqa::BwdParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = out;
+    p.dout = dout;
+    p.lse = lse;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Sq = Sq;
+    p.Sk = Sk;
+    p.G = Hq / Hkv;
+    p.n_hg = B * Hkv;
+    const int rows = gqa::bwd_rows_per_tile();
+    p.n_rb = (int)(((long long)p.G * Sq + rows - 1) / rows);
+    p.n_kb = (Sk + 127) / 128;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    const size_t n = gqa::bwd_workspace_floats(B, Hq, Hkv, Sq);
+    p.ws_d = static_cast<float *>(workspace);
+    p.ws_l = p.ws_d + n;
+    (void)hipGetLastError();
+    return status_from(gqa::launch_bwd_bf16(p, d, causal != 0, cu_seqlens_q != nullptr,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 size_t gqa_attn_decode_workspace_bytes(int B, int Hq, int d, int num_splits) {

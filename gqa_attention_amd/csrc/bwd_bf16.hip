@@ -1,0 +1,626 @@
+// Attention backward, bf16 in / bf16 out, on gfx950 matrix cores.
+//
+// Method (FlashAttention-2 summary, azimuth.plus, paragraph on the backward
+// pass): the probabilities are recomputed from the inputs and the stored row
+// statistic L (so no S or P is ever stored), key/value gradients are
+// accumulated per block of keys, and for grouped heads the key and value
+// gradients are the sums over the query heads that share them. With
+// P = exp(scale q k^T - L), D = rowsum(dO * O):
+//     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+//     dQ = scale dS K,  dK = scale dS^T Q.
+// (D = rowsum(P * dP) because O = P V; the page prints no formulas.)
+//
+// gfx950 mapping (our design, not the pages'):
+//  * bwd_pre: one pass over O and dO gives D and L in log2 units for every
+//    (token, head), written in packed-row order (row rho = pos * G + head in
+//    group) so that a tile of 32 packed rows is 128 contiguous bytes.
+//  * bwd_dkdv: a workgroup owns 128 keys of one K/V head (32 per wave, held
+//    as matrix-core operands in registers) and walks all packed rows of the
+//    G query heads of the group, so the GQA sum of dK and dV happens inside
+//    the accumulators. Per 32-row tile: S = Q K^T and dP = dO V^T (each lane
+//    owns a key), then dV^T += dO^T P and dK^T += Q^T dS, with the
+//    transposed operands dO^T and Q^T read by ds_read_b64_tr_b16.
+//  * bwd_dq: a workgroup owns 128 packed rows (like the forward) and walks
+//    the key tiles: S^T = K Q^T and dP^T = V dO^T (each lane owns a query
+//    row, so L and D are per-lane scalars), dQ^T += K^T dS^T.
+//    The page instead adds dQ atomically from the key-block pass; fp32
+//    atomics at this scale (one update per key block per dQ element) would
+//    cost more than the second pass's recomputation on this chip.
+//  * Q/dO and K/V tiles stream through a 3-slot LDS ring with direct
+//    global->LDS loads issued two tiles ahead, one barrier per tile. Rows are
+//    unpadded with an XOR swizzle of the 16-byte chunk index chosen so that
+//    both the row-slice reads and the transposing reads of a tile are free of
+//    bank conflicts.
+
+#include "device_util.h"
+#include "params.h"
+
+namespace gqa {
+
+namespace {
+
+constexpr int NW = 4;  // wavefronts per workgroup
+constexpr int NTHREADS = 64 * NW;
+constexpr int NSLOT = 3;  // LDS ring depth (tiles two ahead)
+
+// 16-byte chunk slot of chunk c in row r: c ^ swz(r). d = 128 (16 chunks a
+// row): 16 consecutive rows read at one chunk hit 16 distinct slots, and the
+// 4-row x 2-chunk footprint of a transposing read also hits distinct slots.
+// d = 64 (8 chunks, two rows per 256 bytes): the same for rows of equal parity.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Wait until at most N of this wave's loads are outstanding, then meet the
+// other waves (the asm is a compiler memory barrier; no release fence).
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+    if constexpr (N == 0)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (N == 1)
+        asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (N == 2)
+        asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (N == 3)
+        asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (N == 4)
+        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (N == 5)
+        asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+        static_assert(N <= 5, "wait count");
+}
+
+// Start of head group hgl of sequence b in a workspace array (rows padded to
+// a multiple of 4 so that every group starts 16-byte aligned).
+__device__ __forceinline__ int64_t ws_base(const BwdParams &p, int b, int hgl) {
+    return ((int64_t)b * (p.Hq / p.G) + hgl) * (((int64_t)p.Sq * p.G + 3) & ~(int64_t)3);
+}
+
+// ---------------------------------------------------------------------------
+// D = rowsum(dO * O) and L in log2 units, one row per D/8 lanes.
+// ---------------------------------------------------------------------------
+template <int D, bool VARLEN>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
+    constexpr int LPR = D / 8;        // lanes per row, 8 elements each
+    constexpr int RPB = 256 / LPR;    // rows per workgroup
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;  // (b, pos, head)
+    const int c = threadIdx.x % LPR;
+    if (row >= (int64_t)p.B * p.Sq * p.Hq) return;  // uniform over the row's lanes
+    const int head = (int)(row % p.Hq);
+    const int pos = (int)((row / p.Hq) % p.Sq);
+    const int b = (int)(row / ((int64_t)p.Hq * p.Sq));
+    int tok0 = b * p.Sq, Lq = p.Sq;
+    if (VARLEN) {
+        tok0 = p.cu_q[b];
+        Lq = p.cu_q[b + 1] - tok0;
+    }
+    if (pos >= Lq) return;
+    const int64_t off = ((int64_t)(tok0 + pos) * p.Hq + head) * D + 8 * c;
+    const u32x4 ow = *(const u32x4 *)((const __bf16 *)p.o + off);
+    const u32x4 gw = *(const u32x4 *)((const __bf16 *)p.dout + off);
+    const bf16x8 o8 = __builtin_bit_cast(bf16x8, ow), g8 = __builtin_bit_cast(bf16x8, gw);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)o8[e], (float)g8[e], acc);
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (c == 0) {
+        const int64_t li = VARLEN ? (int64_t)(tok0 + pos) * p.Hq + head
+                                  : ((int64_t)b * p.Hq + head) * p.Sq + pos;
+        const float l = p.lse[li];
+        const int hgl = head / p.G;
+        const int64_t wi = ws_base(p, b, hgl) + (int64_t)pos * p.G + (head - hgl * p.G);
+        p.ws_d[wi] = acc;
+        p.ws_l[wi] = l == -INFINITY ? INFINITY : l * kLog2e;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: a workgroup owns 128 keys of one K/V head and walks the packed rows.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2))) void
+bwd_dkdv_kernel(BwdParams p) {
+    constexpr int BR = 32;             // packed rows per tile
+    constexpr int C8 = D / 8;          // 16-byte chunks per row
+    constexpr int DSTEPS = D / 16;     // k-steps of the products over head_dim
+    constexpr int DBLK = D / 32;       // 32-row blocks of dK^T / dV^T
+    constexpr int TILE = BR * D;       // elements of a Q or dO tile
+    constexpr int NDQ = TILE * 2 / 1024 / NW;  // loads per wave per Q (or dO) tile
+    static_assert(NDQ >= 1, "tile too small for one load per wave");
+    constexpr int MISC = 256;          // bytes: L and D of the tile's rows
+    constexpr int SLOT = 2 * TILE * 2 + MISC;  // bytes per ring slot
+    constexpr int NLOAD = 2 * NDQ + 1;         // loads per wave per tile
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[NSLOT * SLOT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, half = lane >> 5;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+    // ---- workgroup -> (sequence, K/V head, key block) ----
+    // Key blocks of one (sequence, K/V head) run back to back on one XCD
+    // when the pairs split evenly over the 8 XCDs (they share Q and dO
+    // through that XCD's L2); lower key blocks (more visible rows under a
+    // causal mask) first.
+    const int pid = blockIdx.x;
+    const int n_grp = p.B * p.Hkv;
+    int grp, kblk;
+    if ((n_grp & 7) == 0) {
+        const int slot = pid >> 3;
+        grp = (slot / p.n_kb) * 8 + (pid & 7);
+        kblk = slot % p.n_kb;
+    } else {
+        grp = pid / p.n_kb;
+        kblk = pid % p.n_kb;
+    }
+    const int b = grp / p.Hkv, kvh = grp - b * p.Hkv;
+    int q_tok0 = b * p.Sq, Lq = p.Sq, k_tok0 = b * p.Sk, Lk = p.Sk;
+    if (VARLEN) {
+        q_tok0 = p.cu_q[b];
+        Lq = p.cu_q[b + 1] - q_tok0;
+        k_tok0 = p.cu_k[b];
+        Lk = p.cu_k[b + 1] - k_tok0;
+    }
+    const int k0 = kblk * 128;
+    if (k0 >= Lk) return;  // uniform over the workgroup
+    const int G = p.G;
+    const int shift = Lk - Lq;
+    const int rows_total = Lq * G;
+    // First packed row that sees key k0 (causal: pos + shift >= k0).
+    int rho_lo = 0;
+    if (CAUSAL) rho_lo = min(rows_total, max(0, k0 - shift) * G);
+    const int t_lo = rho_lo / BR;
+    const int t_hi = (rows_total + BR - 1) / BR;
+
+    // ---- this lane's key and this wave's key range ----
+    const int kk = k0 + 32 * wave + col;
+    const bool key_ok = kk < Lk;
+    const int wk0 = k0 + 32 * wave;             // first key of this wave
+    const int wk1 = min(wk0 + 31, Lk - 1);      // last valid key of this wave
+
+    // K and V rows of this lane's key as B operands (k = head_dim elements
+    // 16 s + 8 half .. +7); keys past the end read the last key and are zeroed.
+    bf16x8 kf[DSTEPS], vf[DSTEPS];
+    {
+        const int kr = key_ok ? kk : Lk - 1;
+        const int64_t off = ((int64_t)(k_tok0 + kr) * p.Hkv + kvh) * D + 8 * half;
+#pragma unroll
+        for (int s = 0; s < DSTEPS; ++s) {
+            const u32x4 a = *(const u32x4 *)((const __bf16 *)p.k + off + 16 * s);
+            const u32x4 c2 = *(const u32x4 *)((const __bf16 *)p.v + off + 16 * s);
+            kf[s] = __builtin_bit_cast(bf16x8, key_ok ? a : u32x4{0u, 0u, 0u, 0u});
+            vf[s] = __builtin_bit_cast(bf16x8, key_ok ? c2 : u32x4{0u, 0u, 0u, 0u});
+        }
+        // Consume the loads before the first DMA (see the forward kernel).
+        u32x4 x = __builtin_bit_cast(u32x4, kf[0]) ^ __builtin_bit_cast(u32x4, vf[0]);
+#pragma unroll
+        for (int s = 1; s < DSTEPS; ++s)
+            x ^= __builtin_bit_cast(u32x4, kf[s]) ^ __builtin_bit_cast(u32x4, vf[s]);
+        asm volatile("" ::"v"(x[0] ^ x[1] ^ x[2] ^ x[3]));
+    }
+
+    // ---- DMA of tile t (packed rows t*32 ..) into a ring slot ----
+    // Q and dO rows: instruction i of wave w fills bytes [1024 (w + NW i), +1024)
+    // of the tile; lane l covers chunk slot (64 (w + NW i) + l) % C8 of row
+    // (64 (w + NW i) + l) / C8. Rows past the end are clamped to the last row.
+    // L and D: lanes 0-1 of every wave fetch L of rows 8 w .. 8 w + 7, lanes
+    // 2-3 their D; the group's arrays are padded, so a tail tile stays inside.
+    int dq_row[NDQ], dq_c[NDQ];
+#pragma unroll
+    for (int i = 0; i < NDQ; ++i) {
+        const int idx = 64 * (wave + NW * i) + lane;
+        dq_row[i] = idx / C8;
+        dq_c[i] = ((idx % C8) ^ swz<D>(dq_row[i])) * 8;
+    }
+    const int hgl = kvh;  // head group = the G query heads of this K/V head
+    const int qh0 = hgl * G;
+    const float *l_src = p.ws_l + ws_base(p, b, hgl);
+    const float *d_src = p.ws_d + ws_base(p, b, hgl);
+    auto dma_tile = [&](int t, int slotn) {
+        unsigned char *base = ring + slotn * SLOT;
+#pragma unroll
+        for (int i = 0; i < NDQ; ++i) {
+            const int rho = min(t * BR + dq_row[i], rows_total - 1);
+            const int pos = rho / G;
+            const int64_t off = ((int64_t)(q_tok0 + pos) * p.Hq + qh0 + (rho - pos * G)) * D + dq_c[i];
+            const uint32_t dst = lds_addr(base) + 1024 * (wave_u + NW * i);
+            lds_dma16_u((const __bf16 *)p.q + off, dst);
+            lds_dma16_u((const __bf16 *)p.dout + off, dst + TILE * 2);
+        }
+        const int r8 = t * BR + 8 * wave + 4 * (lane & 1);
+        const float *src = (lane & 2) ? d_src + r8 : l_src + r8;
+        if (lane < 4) lds_dma16_u(src, lds_addr(base + 2 * TILE * 2) + 64 * wave_u);
+    };
+
+    // Row-slice read (A operand, rows 0..31 of a tile, chunk 2 s + half) and
+    // transposing read (A = X^T: in 16-lane group g, lane j reads row
+    // 4 (g >> 1) + j / 4 (+ 8 for the second read) of a 16-row slot, columns
+    // d0 + 4 (j % 4) .. +3 with d0 = 32 i + 16 (g & 1)).
+    int rs_rd[DSTEPS];
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s) rs_rd[s] = col * D + (((2 * s + half) ^ swz<D>(col)) * 8);
+    // The swizzle depends on row bits 0..3, so the second read (row + 8) has
+    // its own offset; +16 and +32 rows keep the swizzle.
+    const int vj = lane & 15, vg = lane >> 4;
+    const int tr_row = 4 * (vg >> 1) + (vj >> 2);
+    int tr_rd[DBLK], tr_rd8[DBLK];
+#pragma unroll
+    for (int i = 0; i < DBLK; ++i) {
+        const int chunk = 4 * i + 2 * (vg & 1) + ((vj & 3) >> 1);
+        tr_rd[i] = tr_row * D + ((chunk ^ swz<D>(tr_row)) * 8) + 4 * (vj & 1);
+        tr_rd8[i] = (tr_row + 8) * D + ((chunk ^ swz<D>(tr_row + 8)) * 8) + 4 * (vj & 1);
+    }
+
+    const float c = p.scale_log2;
+    f32x16 dkacc[DBLK], dvacc[DBLK];
+#pragma unroll
+    for (int i = 0; i < DBLK; ++i) {
+        dkacc[i] = f32x16{};
+        dvacc[i] = f32x16{};
+    }
+
+    // Does this wave's key range meet tile t? Is every (row, key) pair of the
+    // tile visible (no element mask needed)?
+    auto wave_needs = [&](int t) {
+        if (wk0 >= Lk) return false;
+        if (!CAUSAL) return true;
+        const int last_row = min(t * BR + BR, rows_total) - 1;
+        return last_row / G + shift >= wk0;
+    };
+    auto tile_full = [&](int t) {
+        if (t * BR + BR > rows_total || wk1 < wk0 + 31) return false;
+        if (!CAUSAL) return true;
+        return (t * BR) / G + shift >= wk0 + 31;
+    };
+
+    if (t_lo < t_hi) {
+        dma_tile(t_lo, 0);
+        dma_tile(t_lo + 1, 1);
+    }
+    for (int t = t_lo; t < t_hi; ++t) {
+        const int it = t - t_lo;
+        wait_barrier<NLOAD>();  // tile t has landed; every wave is done with tile t-1
+        dma_tile(t + 2, (it + 2) % NSLOT);
+        if (!wave_needs(t)) continue;
+        const unsigned char *base = ring + (it % NSLOT) * SLOT;
+        const __bf16 *qt = (const __bf16 *)base;
+        const __bf16 *gt = (const __bf16 *)(base + TILE * 2);
+        const float *misc = (const float *)(base + 2 * TILE * 2);
+
+        // S = Q K^T and dP = dO V^T: rows 8 (j/4) + 4 half + j%4, key col.
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < DSTEPS; ++s) {
+            const bf16x8 a = *(const bf16x8 *)(qt + rs_rd[s]);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[s], sacc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int s = 0; s < DSTEPS; ++s) {
+            const bf16x8 a = *(const bf16x8 *)(gt + rs_rd[s]);
+            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[s], dpacc, 0, 0, 0);
+        }
+        // P = 2^(s c - L), dS = P (dP - D); masked pairs and rows past the end
+        // give P = 0. B operands for k-step h2: rows 16 h2 + 8 (e/4) + 4 half + e%4.
+        const bool full = tile_full(t);
+        bf16x8 pf[2], dsf[2];
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            const f32x4 lv = *(const f32x4 *)(misc + 16 * blk + 4 * half);
+            const f32x4 dv4 = *(const f32x4 *)(misc + 16 * blk + 8 + 4 * half);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * blk + e;
+                float pv = fast_exp2(fmaf(sacc[j], c, -lv[e]));
+                float ds = pv * (dpacc[j] - dv4[e]);
+                if (!full) {
+                    // rows past the end carry arbitrary L and D: select, not scale
+                    const int rho = t * BR + 8 * blk + 4 * half + e;
+                    const bool vis = rho < rows_total && key_ok &&
+                                     (!CAUSAL || kk <= rho / G + shift);
+                    pv = vis ? pv : 0.f;
+                    ds = vis ? ds : 0.f;
+                }
+                pf[blk >> 1][4 * (blk & 1) + e] = (__bf16)pv;
+                dsf[blk >> 1][4 * (blk & 1) + e] = (__bf16)ds;
+            }
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS (A operands by transposing reads).
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int i = 0; i < DBLK; ++i) {
+                const int o = 16 * h2 * D + tr_rd[i], o8 = 16 * h2 * D + tr_rd8[i];
+                const u32x2 g0 = lds_read_tr16(gt + o), g1 = lds_read_tr16(gt + o8);
+                const u32x2 q0 = lds_read_tr16(qt + o), q1 = lds_read_tr16(qt + o8);
+                const bf16x8 ag = __builtin_bit_cast(bf16x8, u32x4{g0[0], g0[1], g1[0], g1[1]});
+                const bf16x8 aq = __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]});
+                dvacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pf[h2], dvacc[i], 0, 0, 0);
+                dkacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsf[h2], dkacc[i], 0, 0, 0);
+            }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the (unused) tail loads
+
+    // ---- write dK = scale dK^T^T and dV: lane owns key kk, head_dim
+    // elements 32 i + 8 g + 4 half .. +3 ----
+    if (!key_ok) return;
+    const int64_t off = ((int64_t)(k_tok0 + kk) * p.Hkv + kvh) * D + 4 * half;
+    __bf16 *dkrow = (__bf16 *)p.dk + off;
+    __bf16 *dvrow = (__bf16 *)p.dv + off;
+#pragma unroll
+    for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            bf16x4 wk, wv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                wk[e] = (__bf16)(dkacc[i][4 * g + e] * p.scale);
+                wv[e] = (__bf16)dvacc[i][4 * g + e];
+            }
+            *(u32x2 *)(dkrow + i * 32 + 8 * g) = __builtin_bit_cast(u32x2, wk);
+            *(u32x2 *)(dvrow + i * 32 + 8 * g) = __builtin_bit_cast(u32x2, wv);
+        }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: a workgroup owns 128 packed rows and walks the key tiles.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2))) void
+bwd_dq_kernel(BwdParams p) {
+    constexpr int BM = 32 * NW;            // packed rows per workgroup
+    constexpr int BN = D == 128 ? 32 : 64;  // keys per tile
+    constexpr int KB = BN / 32;
+    constexpr int C8 = D / 8;
+    constexpr int DSTEPS = D / 16;
+    constexpr int DBLK = D / 32;
+    constexpr int TILE = BN * D;
+    constexpr int NDK = TILE * 2 / 1024 / NW;  // loads per wave per K (or V) tile
+    static_assert(NDK >= 1, "tile too small for one load per wave");
+    constexpr int NLOAD = 2 * NDK;
+    __shared__ __attribute__((aligned(1024))) __bf16 ring[NSLOT * 2 * TILE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, half = lane >> 5;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+    // ---- workgroup -> (head group, row tile), as the forward ----
+    const int pid = blockIdx.x;
+    int hg, rank;
+    if ((p.n_hg & 7) == 0) {
+        const int slot = pid >> 3;
+        hg = (slot / p.n_rb) * 8 + (pid & 7);
+        rank = slot % p.n_rb;
+    } else {
+        hg = pid / p.n_rb;
+        rank = pid % p.n_rb;
+    }
+    const int rb = CAUSAL ? (p.n_rb - 1 - rank) : rank;
+    const int b = hg / p.Hkv, kvh = hg - b * p.Hkv;
+    const int G = p.G, qh0 = kvh * G;
+    int q_tok0 = b * p.Sq, Lq = p.Sq, k_tok0 = b * p.Sk, Lk = p.Sk;
+    if (VARLEN) {
+        q_tok0 = p.cu_q[b];
+        Lq = p.cu_q[b + 1] - q_tok0;
+        k_tok0 = p.cu_k[b];
+        Lk = p.cu_k[b + 1] - k_tok0;
+    }
+    const int rows_total = Lq * G;
+    const int row0 = rb * BM;
+    if (row0 >= rows_total) return;  // uniform over the workgroup
+    const int shift = Lk - Lq;
+    int kend = Lk;
+    if (CAUSAL) {
+        const int last = min(row0 + BM, rows_total) - 1;
+        kend = min(Lk, last / G + 1 + shift);
+    }
+    const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+    // ---- this lane's query row ----
+    const int rho = row0 + wave * 32 + col;
+    const bool row_ok = rho < rows_total;
+    const int pos = rho / G;
+    const int head = qh0 + (rho - pos * G);
+    const int row_kend = CAUSAL ? min(Lk, pos + 1 + shift) : Lk;
+    const int wr0 = row0 + wave * 32;
+    const bool wave_live = wr0 < rows_total;
+    const int wr1 = min(wr0 + 31, rows_total - 1);
+    int wave_kend = Lk, wave_kfull = Lk;
+    if (CAUSAL) {
+        wave_kend = min(Lk, wr1 / G + 1 + shift);
+        wave_kfull = min(Lk, wr0 / G + 1 + shift);
+    }
+
+    // Per-row statistics and the Q^T / dO^T fragments (B operands).
+    float lrow = INFINITY, drow = 0.f;
+    bf16x8 qf[DSTEPS], gf[DSTEPS];
+    {
+        if (row_ok) {
+            const int64_t wi = ws_base(p, b, kvh) + rho;
+            lrow = p.ws_l[wi];
+            drow = p.ws_d[wi];
+        }
+        const int qpos = row_ok ? pos : Lq - 1;
+        const int qhead = row_ok ? head : qh0;
+        const int64_t off = ((int64_t)(q_tok0 + qpos) * p.Hq + qhead) * D + 8 * half;
+#pragma unroll
+        for (int s = 0; s < DSTEPS; ++s) {
+            const u32x4 a = *(const u32x4 *)((const __bf16 *)p.q + off + 16 * s);
+            const u32x4 g2 = *(const u32x4 *)((const __bf16 *)p.dout + off + 16 * s);
+            qf[s] = __builtin_bit_cast(bf16x8, row_ok ? a : u32x4{0u, 0u, 0u, 0u});
+            gf[s] = __builtin_bit_cast(bf16x8, row_ok ? g2 : u32x4{0u, 0u, 0u, 0u});
+        }
+        u32x4 x = __builtin_bit_cast(u32x4, qf[0]) ^ __builtin_bit_cast(u32x4, gf[0]);
+#pragma unroll
+        for (int s = 1; s < DSTEPS; ++s)
+            x ^= __builtin_bit_cast(u32x4, qf[s]) ^ __builtin_bit_cast(u32x4, gf[s]);
+        const uint32_t y = x[0] ^ x[1] ^ x[2] ^ x[3] ^ __builtin_bit_cast(uint32_t, lrow) ^
+                           __builtin_bit_cast(uint32_t, drow);
+        asm volatile("" ::"v"(y));
+    }
+
+    // ---- DMA of key tile t of K and V into a ring slot ----
+    int dk_row[NDK], dk_c[NDK];
+#pragma unroll
+    for (int i = 0; i < NDK; ++i) {
+        const int idx = 64 * (wave + NW * i) + lane;
+        dk_row[i] = idx / C8;
+        dk_c[i] = ((idx % C8) ^ swz<D>(dk_row[i])) * 8;
+    }
+    const int64_t kv_stride = (int64_t)p.Hkv * D;
+    const __bf16 *kbase = (const __bf16 *)p.k + ((int64_t)k_tok0 * p.Hkv + kvh) * D;
+    const __bf16 *vbase = (const __bf16 *)p.v + ((int64_t)k_tok0 * p.Hkv + kvh) * D;
+    auto dma_tile = [&](int t, int slotn) {
+        __bf16 *kd = ring + slotn * 2 * TILE;
+#pragma unroll
+        for (int i = 0; i < NDK; ++i) {
+            const int64_t roff = (int64_t)min(t * BN + dk_row[i], kend - 1) * kv_stride + dk_c[i];
+            const uint32_t dst = lds_addr(kd) + 1024 * (wave_u + NW * i);
+            lds_dma16_u(kbase + roff, dst);
+            lds_dma16_u(vbase + roff, dst + TILE * 2);
+        }
+    };
+
+    int rs_rd[DSTEPS];
+#pragma unroll
+    for (int s = 0; s < DSTEPS; ++s) rs_rd[s] = col * D + (((2 * s + half) ^ swz<D>(col)) * 8);
+    // The swizzle depends on row bits 0..3, so the second read (row + 8) has
+    // its own offset; +16 and +32 rows keep the swizzle.
+    const int vj = lane & 15, vg = lane >> 4;
+    const int tr_row = 4 * (vg >> 1) + (vj >> 2);
+    int tr_rd[DBLK], tr_rd8[DBLK];
+#pragma unroll
+    for (int i = 0; i < DBLK; ++i) {
+        const int chunk = 4 * i + 2 * (vg & 1) + ((vj & 3) >> 1);
+        tr_rd[i] = tr_row * D + ((chunk ^ swz<D>(tr_row)) * 8) + 4 * (vj & 1);
+        tr_rd8[i] = (tr_row + 8) * D + ((chunk ^ swz<D>(tr_row + 8)) * 8) + 4 * (vj & 1);
+    }
+
+    const float c = p.scale_log2;
+    f32x16 dqacc[DBLK];
+#pragma unroll
+    for (int i = 0; i < DBLK; ++i) dqacc[i] = f32x16{};
+    auto wave_needs = [&](int t) { return wave_live && t * BN < wave_kend; };
+
+    if (ntiles > 0) {
+        dma_tile(0, 0);
+        dma_tile(1, 1);
+    }
+    for (int t = 0; t < ntiles; ++t) {
+        wait_barrier<NLOAD>();  // tile t has landed; every wave is done with tile t-1
+        dma_tile(t + 2, (t + 2) % NSLOT);
+        if (!wave_needs(t)) continue;
+        const __bf16 *kt = ring + (t % NSLOT) * 2 * TILE;
+        const __bf16 *vt = kt + TILE;
+        // S^T = K Q^T, dP^T = V dO^T: keys kb*32 + 8 (j/4) + 4 half + j%4, row col.
+        f32x16 sacc[KB], dpacc[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            sacc[kb] = f32x16{};
+            dpacc[kb] = f32x16{};
+#pragma unroll
+            for (int s = 0; s < DSTEPS; ++s) {
+                const bf16x8 a = *(const bf16x8 *)(kt + kb * 32 * D + rs_rd[s]);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
+            }
+#pragma unroll
+            for (int s = 0; s < DSTEPS; ++s) {
+                const bf16x8 a = *(const bf16x8 *)(vt + kb * 32 * D + rs_rd[s]);
+                dpacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, gf[s], dpacc[kb], 0, 0, 0);
+            }
+        }
+        // dS^T = P^T (dP^T - D), P^T = 2^(s c - L); masked keys give P = 0.
+        const bool full = (t + 1) * BN <= wave_kfull;
+        bf16x8 dsf[KB][2];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = 8 * h2 + e;
+                    float pv = fast_exp2(fmaf(sacc[kb][j], c, -lrow));
+                    if (!full) {
+                        const int key = t * BN + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+                        pv = key < row_kend ? pv : 0.f;
+                    }
+                    dsf[kb][h2][e] = (__bf16)(pv * (dpacc[kb][j] - drow));
+                }
+        // dQ^T += K^T dS^T (A = K^T by transposing reads).
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < DBLK; ++i) {
+                    const __bf16 *kp = kt + (kb * 32 + 16 * h2) * D;
+                    const u32x2 lo = lds_read_tr16(kp + tr_rd[i]), hi = lds_read_tr16(kp + tr_rd8[i]);
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                    dqacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[kb][h2], dqacc[i], 0, 0, 0);
+                }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // ---- write dQ = scale dQ^T^T: lane owns row rho ----
+    if (!row_ok) return;
+    __bf16 *qrow = (__bf16 *)p.dq + ((int64_t)(q_tok0 + pos) * p.Hq + head) * D + 4 * half;
+#pragma unroll
+    for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            bf16x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = (__bf16)(dqacc[i][4 * g + e] * p.scale);
+            *(u32x2 *)(qrow + i * 32 + 8 * g) = __builtin_bit_cast(u32x2, w);
+        }
+}
+
+template <int D, bool CAUSAL, bool VARLEN>
+hipError_t launch_t(const BwdParams &p, hipStream_t s) {
+    constexpr int RPB = 256 / (D / 8);
+    const long long pre_rows = (long long)p.B * p.Sq * p.Hq;
+    if (pre_rows > 0) {
+        hipLaunchKernelGGL((bwd_pre_kernel<D, VARLEN>), dim3((unsigned)((pre_rows + RPB - 1) / RPB)),
+                           dim3(256), 0, s, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const long long kv_grid = (long long)p.B * p.Hkv * p.n_kb;
+    if (kv_grid > 0) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)kv_grid),
+                           dim3(NTHREADS), 0, s, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const long long q_grid = (long long)p.n_hg * p.n_rb;
+    if (q_grid > 0) {
+        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)q_grid),
+                           dim3(NTHREADS), 0, s, p);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+int bwd_rows_per_tile() { return 32 * NW; }
+
+hipError_t launch_bwd_bf16(const BwdParams &p, int d, bool causal, bool varlen, hipStream_t s) {
+#define GQA_CASE(D_, C_, V_) \
+    if (d == D_ && causal == C_ && varlen == V_) return launch_t<D_, C_, V_>(p, s);
+    GQA_CASE(64, false, false)
+    GQA_CASE(64, true, false)
+    GQA_CASE(64, false, true)
+    GQA_CASE(64, true, true)
+    GQA_CASE(128, false, false)
+    GQA_CASE(128, true, false)
+    GQA_CASE(128, false, true)
+    GQA_CASE(128, true, true)
+#undef GQA_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gqa

@@ -61,6 +61,16 @@ __device__ __forceinline__ void lds_dma16(const void *gptr, uint32_t lds_base) {
                  : "s"(lds_base), "v"(gptr)
                  : "memory", "m0");
 }
+// The same for an LDS address the compiler may hold in a vector register
+// (it must still be the same in every lane): readfirstlane moves it to an
+// SGPR for M0.
+__device__ __forceinline__ void lds_dma16_u(const void *gptr, uint32_t lds_base) {
+    const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_base);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(m), "v"(gptr)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;

@@ -50,11 +50,32 @@ struct DecodeParams {
     float *ws_lse;               // [num_splits, B*Hq] fp32
 };
 
+// One backward launch (three kernels: row statistics, dK/dV, dQ). The
+// workspace holds two fp32 arrays in packed-row order: for sequence b and
+// head group g (the G query heads of one K/V head), row rho = pos * G + r is
+// element (b * (Hq / G) + g) * R + rho with R = Sq * G rounded up to a
+// multiple of 4; each array is followed by 128 spare floats so that whole
+// 32-row tiles (and the prefetch two tiles ahead) can be fetched.
+struct BwdParams {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;
+    void *dq, *dk, *dv;
+    const int32_t *cu_q, *cu_k;  // both null for fixed length
+    int B, Hq, Hkv, Sq, Sk, G;   // Sq / Sk: lengths, or the maxima for variable length
+    int n_hg;                    // B * Hkv head groups (dQ grid)
+    int n_rb;                    // 128-row tiles per head group (dQ grid)
+    int n_kb;                    // 128-key blocks per sequence (dK/dV grid)
+    float scale, scale_log2;
+    float *ws_d;                 // rowsum(dO * O)
+    float *ws_l;                 // LSE in log2 units, +inf for rows that see no key
+};
+
 // Launchers (one per kernel family). Each returns a hipError_t.
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, bool causal, bool varlen, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams &p, int d, bool causal, bool varlen, bool split,
                           hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeParams &p, int d, bool paged, bool fp8_kv, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdParams &p, int d, bool causal, bool varlen, hipStream_t s);
 hipError_t launch_decode_combine(const float *ws_o, const float *ws_lse, void *out, float *lse,
                                  int rows, int num_splits, int d, bool out_bf16, hipStream_t s);
 

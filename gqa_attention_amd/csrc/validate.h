@@ -13,6 +13,7 @@ namespace gqa {
 
 constexpr int kMaxSplits = 64;
 constexpr int kSplitAlign = 64;  // split chunk granularity (keys)
+constexpr int kBwdPadFloats = 128;  // spare floats after each backward statistics array
 
 inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -80,6 +81,35 @@ inline int validate_decode(const void *q, const void *kc, const void *vc, const 
         if (!ws || !aligned(ws, 16)) return GQA_EWORKSPACE;
         if (ws_bytes < decode_workspace_bytes(B, Hq, d, num_splits)) return GQA_EWORKSPACE;
     }
+    return GQA_OK;
+}
+
+// Row statistics of the backward: 2 arrays of B * Hq * R floats (R = Sq * G
+// rounded up to 4 per head group) plus kBwdPad floats each.
+inline size_t bwd_workspace_floats(int B, int Hq, int Hkv, int Sq) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Sq < 0) return 0;
+    const long long G = Hq / Hkv;
+    const long long rows = (long long)B * Hkv * (((long long)Sq * G + 3) & ~3LL);
+    return (size_t)(rows + kBwdPadFloats);
+}
+inline size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq) {
+    const size_t n = bwd_workspace_floats(B, Hq, Hkv, Sq);
+    return n ? 2 * n * sizeof(float) : 0;
+}
+
+inline int validate_bwd(const void *q, const void *k, const void *v, const void *out,
+                        const float *lse, const void *dout, const void *dq, const void *dk,
+                        const void *dv, int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale,
+                        const int32_t *cu_q, const int32_t *cu_k, const void *ws,
+                        size_t ws_bytes, int dtype) {
+    const int rc = validate_fwd(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, d, scale, cu_q, cu_k, dtype);
+    if (rc != GQA_OK) return rc;
+    if (dtype != GQA_DTYPE_BF16) return GQA_EUNSUPPORTED;
+    if (!dout || !dq || !dk || !dv) return GQA_EINVAL;
+    if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+        return GQA_EINVAL;
+    if (!ws || !aligned(ws, 16) || ws_bytes < bwd_workspace_bytes(B, Hq, Hkv, Sq))
+        return GQA_EWORKSPACE;
     return GQA_OK;
 }
 

@@ -92,6 +92,41 @@ int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *
                  int dtype, void *stream);
 
 /*
+ * gqa_attn_bwd_workspace_bytes - size of the caller-owned workspace of
+ * gqa_attn_bwd for B sequences, Hq query heads (of Hkv K/V heads) and Sq
+ * query rows (the largest per-sequence length for variable length): two
+ * fp32 row statistics per (sequence, head, row) plus padding. Returns 0 for
+ * invalid sizes.
+ */
+size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq);
+
+/*
+ * gqa_attn_bwd - gradients of gqa_attn_fwd (FlashAttention-2 summary,
+ * backward-pass paragraph: probabilities recomputed from the inputs and the
+ * stored LSE; key/value gradients accumulated per key block and summed over
+ * the query heads that share each K/V head).
+ *
+ * Inputs: q, k, v, out and lse exactly as given to / returned by
+ * gqa_attn_fwd with the same sizes, causal flag, scale and cu_seqlens, plus
+ * dout (the gradient of out, same layout as out). Outputs: dq (layout of q),
+ * dk, dv (layout of k, v), overwritten (not accumulated). bf16 only
+ * (dtype GQA_DTYPE_BF16; GQA_DTYPE_FP32 gives GQA_EUNSUPPORTED).
+ *   dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO * O)),
+ *   dQ = scale dS K, dK = scale dS^T Q, P = exp(scale q k^T - LSE),
+ * with dK, dV of K/V head g summed over query heads h with h / G = g.
+ * Keys that no query sees get dK = dV = 0; rows that see no key get dQ = 0.
+ * workspace: device memory of at least gqa_attn_bwd_workspace_bytes(B, Hq,
+ * Hkv, Sq) bytes, 16-byte aligned, contents ignored and overwritten.
+ * Errors: as gqa_attn_fwd, plus GQA_EWORKSPACE for a missing or short
+ * workspace.
+ */
+int gqa_attn_bwd(const void *q, const void *k, const void *v, const void *out, const float *lse,
+                 const void *dout, void *dq, void *dk, void *dv, int B, int Hq, int Hkv, int Sq,
+                 int Sk, int d, float scale, int causal, const int32_t *cu_seqlens_q,
+                 const int32_t *cu_seqlens_k, void *workspace, size_t workspace_bytes, int dtype,
+                 void *stream);
+
+/*
  * gqa_attn_decode_workspace_bytes - size of the caller-owned workspace that
  * gqa_attn_decode needs for num_splits partial results (fp32 normalised
  * partial outputs [num_splits, B*Hq, d] followed by fp32 partial LSEs

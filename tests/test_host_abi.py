@@ -30,7 +30,8 @@ def declared_functions():
 
 
 def test_header_declares_the_api():
-    assert declared_functions() == ["gqa_attn_decode", "gqa_attn_decode_ex",
+    assert declared_functions() == ["gqa_attn_bwd", "gqa_attn_bwd_workspace_bytes",
+                                    "gqa_attn_decode", "gqa_attn_decode_ex",
                                     "gqa_attn_decode_num_splits",
                                     "gqa_attn_decode_workspace_bytes", "gqa_attn_fwd",
                                     "gqa_attn_strerror"]
@@ -224,3 +225,49 @@ def test_decode_num_splits_rule():
     for bad in [(0, 32, 8, 128, 10), (1, 30, 8, 128, 10), (1, 32, 8, 96, 10),
                 (1, 32, 8, 128, 0), (1, 32, 8, 128, 10, -2)]:
         assert f(*bad) == 0, bad
+
+
+def bwd_call(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             B=2, Hq=8, Hkv=2, Sq=100, Sk=120, d=128, scale=0.1, causal=1, cu_q=None, cu_k=None,
+             ws=FAKE, ws_bytes=1 << 30, dtype=0, stream=None)
+    a.update(kw)
+    return ga.lib().gqa_attn_bwd(
+        a["q"], a["k"], a["v"], a["out"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"], a["B"],
+        a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"], a["scale"], a["causal"], a["cu_q"],
+        a["cu_k"], a["ws"], a["ws_bytes"], a["dtype"], a["stream"])
+
+
+BWD_ERRORS = [
+    (dict(q=None), ga.GQA_EINVAL),
+    (dict(dout=None), ga.GQA_EINVAL),
+    (dict(dq=None), ga.GQA_EINVAL),
+    (dict(dk=None), ga.GQA_EINVAL),
+    (dict(dv=None), ga.GQA_EINVAL),
+    (dict(dv=FAKE + 8), ga.GQA_EINVAL),
+    (dict(d=96), ga.GQA_EUNSUPPORTED),
+    (dict(dtype=1), ga.GQA_EUNSUPPORTED),      # fp32 has no backward
+    (dict(Hq=9), ga.GQA_EINVAL),
+    (dict(Sq=0), ga.GQA_EINVAL),
+    (dict(scale=0.0), ga.GQA_EINVAL),
+    (dict(ws=None), ga.GQA_EWORKSPACE),
+    (dict(ws=FAKE + 8), ga.GQA_EWORKSPACE),
+    (dict(ws_bytes=1000), ga.GQA_EWORKSPACE),
+]
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", BWD_ERRORS, ids=lambda x: str(x))
+def test_bwd_argument_errors(kw, code):
+    assert bwd_call(**kw) == code
+
+
+@needs_lib
+def test_bwd_workspace_size():
+    f = ga.bwd_workspace_bytes
+    # two fp32 arrays of B * Hkv * round4(Sq * G) rows plus 128 spare floats each
+    assert f(2, 8, 2, 100) == 2 * 4 * (2 * 2 * 400 + 128)
+    assert f(1, 12, 12, 77) == 2 * 4 * (12 * 80 + 128)
+    assert f(0, 8, 2, 10) == 0 and f(1, 9, 2, 10) == 0 and f(1, 8, 2, -1) == 0
+    need = f(2, 8, 2, 100)
+    assert bwd_call(ws_bytes=need - 1) == ga.GQA_EWORKSPACE
