@@ -109,6 +109,51 @@ def attention_grad(q, k, v, do, scale: float, causal: bool,
     return dq, dk, dv
 
 
+def attention_grad_sampled(q, k, v, do, scale: float, causal: bool, rows, keys):
+    """The same gradients evaluated only at chosen rows (dq) and keys (dk, dv),
+    for full-size workloads where materialising every P is too costly.
+
+    Fixed length only. rows: (b, pos, head) triples -> dq [n, d]; keys:
+    (b, key, kv_head) triples -> dk, dv [m, d]. Every row's LSE and
+    D = rowsum(dO * O) come from the plain forward definition
+    (``oracle.gqa.attention``); then, per the chain rule above,
+        dq_i = scale sum_j P_ij (dP_ij - D_i) k_j
+        dk_j = scale sum over rows i and query heads h of group(j) of
+               P_ij (dP_ij - D_i) q_i,    dv_j = sum of P_ij dO_i.
+    """
+    scale = float(np.float32(scale))
+    q, k, v, do = (_gqa.as_f64(x) for x in (q, k, v, do))
+    o, lse = _gqa.attention(q, k, v, scale, causal)        # [B, Sq, Hq, d], [B, Hq, Sq]
+    dsum = (do * o).sum(axis=-1)                             # [B, Sq, Hq]
+    B, sq, hq, d = q.shape
+    sk, hkv = k.shape[1], k.shape[2]
+    G = hq // hkv
+    dq = np.zeros((len(rows), d))
+    for n, (b, i, h) in enumerate(rows):
+        g = _gqa.kv_head_of(h, hq, hkv)
+        vis = _gqa.visible(sq, sk, causal)[i]
+        s_row = scale * (k[b, :, g] @ q[b, i, h])
+        p = np.where(vis, np.exp(s_row - lse[b, h, i]), 0.0) if np.isfinite(lse[b, h, i]) \
+            else np.zeros(sk)
+        dp = v[b, :, g] @ do[b, i, h]
+        dq[n] = scale * ((p * (dp - dsum[b, i, h])) @ k[b, :, g])
+    dk = np.zeros((len(keys), d))
+    dv = np.zeros((len(keys), v.shape[-1]))
+    vis_all = _gqa.visible(sq, sk, causal)
+    for n, (b, j, g) in enumerate(keys):
+        for h in range(g * G, (g + 1) * G):
+            s_col = scale * (q[b, :, h] @ k[b, j, g])
+            l = lse[b, h]
+            live = vis_all[:, j] & np.isfinite(l)
+            p = np.zeros(sq)
+            p[live] = np.exp(s_col[live] - l[live])
+            dp = do[b, :, h] @ v[b, j, g]
+            ds = p * (dp - dsum[b, :, h])
+            dk[n] += scale * (ds @ q[b, :, h])
+            dv[n] += p @ do[b, :, h]
+    return dq, dk, dv
+
+
 def attention_grad_flops(lq: int, lk: int, hq: int, d: int, causal: bool) -> int:
     """Algorithmic flops of the backward of one sequence: five products per
     visible (query, key) pair and query head (S, dP, dV, dQ, dK), each a

@@ -116,11 +116,9 @@ def test_bwd_varlen(case, d):
     print(case, d, errs)
 
 
-def test_bwd_keys_no_query_sees_get_zero():
-    """Causal with Lq < Lk: every key is seen by the last row, so nothing is
-    zero there; with Lq > Lk no key is unseen either. A key block past every
-    row's reach exists only with Lq = 0, covered by the varlen cases; here
-    the unseen rows of Lq > Lk must get dq = 0 exactly."""
+def test_bwd_rows_without_keys_get_zero_dq():
+    """Causal with Lq > Lk: the first Lq - Lk rows see no key; their dq is
+    exactly zero and the other rows' is not."""
     w = gqa_inputs.fixed(1, 4, 2, 150, 40, 64, seed=9, causal=True)
     dq, _, _ = run_bwd(w, _dout(w, 79))
     assert torch.all(dq[0, :110] == 0)

@@ -222,3 +222,17 @@ def test_planted_mistake_is_caught(name, monkeypatch):
         if not ok:
             failed.append(p.__name__)
     assert failed, f"mutation {name} slipped past every pin"
+
+
+def test_sampled_gradients_match_full():
+    """The row/key-sampled evaluator agrees with the full oracle."""
+    for causal in (False, True):
+        w = gi.fixed(2, 6, 2, 9, 7, 4, seed=31, dtype=torch.float32, causal=causal)
+        do = _do_like(w, 8)
+        dq, dk, dv = _grads(w, do)
+        rows = [(0, 0, 0), (1, 8, 5), (0, 4, 3), (1, 1, 2)]
+        keys = [(0, 0, 0), (1, 6, 1), (0, 3, 1)]
+        sq, sk, sv = ob.attention_grad_sampled(w.q, w.k, w.v, do, w.scale, causal, rows, keys)
+        assert _close(sq, [dq[b, i, h] for b, i, h in rows], 1e-12)
+        assert _close(sk, [dk[b, j, g] for b, j, g in keys], 1e-12)
+        assert _close(sv, [dv[b, j, g] for b, j, g in keys], 1e-12)
