@@ -12,10 +12,11 @@ Printed: ONE JSON line with the metric, the dominant kernel's roofline
 launch stream), the CPU oracle timed on a bounded sample (rank 0, N = 1) and,
 under "extra", the other workloads (8192-token causal GQA prefill, split-KV
 decode at num_splits 1/2/4/8, packed variable-length causal GQA, tiny fp32,
-and decode over general caches: ragged paged bf16 and fp8, sliding window).
+the backward pass on the encoder, prefill and varlen workloads, and decode over
+general caches: ragged paged bf16 and fp8, sliding window).
 
 Flop count: 4 * d per visible (query, key) pair per query head (two products,
-multiply-add = 2 flops). Decode bytes: the K and V cache bytes read,
+multiply-add = 2 flops); the backward counts 10 * d (five products). Decode bytes: the K and V cache bytes read,
 2 * B * Sk * Hkv * d * 2; for a general cache, the visible keys of every
 sequence x Hkv x d x element size x 2.
 """
@@ -177,6 +178,34 @@ def bench_decode(torch, ga, w, ns, steps, warmup, sets):
     return dict(bytes=kv_bytes, wall=wall, avg_ms=avg_ms)
 
 
+def bench_bwd(torch, ga, w, steps, warmup):
+    """Time gqa_attn_bwd alone (its O and LSE come from one forward first).
+    Flops: 10 d per visible (query, key) pair per query head (the five
+    products S, dP, dV, dQ, dK)."""
+    q, k, v = w.q.cuda(), w.k.cuda(), w.v.cuda()
+    kw = dict(causal=w.causal, scale=w.scale)
+    if w.varlen:
+        kw.update(cu_seqlens_q=w.cu_seqlens_q.cuda(), cu_seqlens_k=w.cu_seqlens_k.cuda(),
+                  max_seqlen_q=w.max_seqlen_q, max_seqlen_k=w.max_seqlen_k)
+    o, lse = ga.fwd(q, k, v, **kw)
+    g = torch.Generator().manual_seed(20_000)
+    do = torch.randn(w.q.shape, generator=g).to(w.q.dtype).cuda()
+    plan = ga.BwdPlan(q, k, v, o, lse, do, **kw)
+    wall, avg_ms = run_timed(torch, lambda i: plan.run(), steps, warmup)
+    flops = fwd_flops_of(w) // 4 * 10
+    return dict(flops=flops, wall=wall, avg_ms=avg_ms)
+
+
+def fwd_flops_of(w) -> int:
+    if w.varlen:
+        cu = w.cu_seqlens_q.tolist()
+        ck = w.cu_seqlens_k.tolist()
+        return sum(fwd_flops(cu[b + 1] - cu[b], ck[b + 1] - ck[b], w.q.shape[1], w.q.shape[2],
+                             w.causal) for b in range(len(cu) - 1))
+    B, sq, hq, d = w.q.shape
+    return B * fwd_flops(sq, w.k.shape[1], hq, d, w.causal)
+
+
 def cache_kv_bytes(wc) -> int:
     """K and V bytes a decode over a general cache must read: the visible keys
     of every sequence x Hkv x d x element size, for K and for V."""
@@ -298,6 +327,8 @@ def main():
                              "decode_ragged_paged", "decode_ragged_paged_fp8",
                              "decode_sliding_window"])
     ap.add_argument("--num-splits", type=int, default=1, help="decode workload only")
+    ap.add_argument("--pass", dest="pass_", choices=["forward", "backward"], default="forward",
+                    help="backward: time gqa_attn_bwd on a forward workload (prints that line only)")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-counters", metavar="PMC_DIR",
@@ -349,6 +380,26 @@ def main():
         return rc, {"workload": wc.name, "kernel": kern, "num_splits": ns,
                     "kv_gbs": round(gbs, 1), "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
                     "ms_per_call": round(rc["avg_ms"], 5), "kv_bytes": rc["bytes"]}
+
+    if args.pass_ == "backward":
+        w = loaders[args.workload]()
+        if w.decode or w.q.dtype != torch.bfloat16:
+            print("the backward pass is timed on the bf16 forward workloads", file=sys.stderr)
+            sys.exit(2)
+        r = bench_bwd(torch, ga, w, args.steps, args.warmup)
+        tf = r["flops"] / (r["avg_ms"] * 1e-3) / 1e12
+        line = {"metric": METRIC, "value": round(r["flops"] * args.steps / r["wall"] / 1e12, 3),
+                "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": round(r["wall"] * 1e3 / args.steps, 5), "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                "config": {"workload": w.name, "pass": "backward",
+                           "gflop_per_step": round(r["flops"] / 1e9, 3)},
+                "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                             "traffic": None, "kernel": "bwd (pre + dkdv + dq)",
+                             "launch_ms": round(r["avg_ms"], 5)}}
+        print(json.dumps(line))
+        return
 
     if args.workload in gqa_inputs.CACHE_NAMED:
         w = gqa_inputs.CACHE_NAMED[args.workload]()
@@ -436,6 +487,17 @@ def main():
                               "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
                               "ms_per_call": round(rd["avg_ms"], 5)})
             del wd
+        for name in ["bert_base_encoder", "llama31_8b_prefill", "varlen_packed_causal"]:
+            wb = loaders[name]()
+            rb = bench_bwd(torch, ga, wb, 10, 2)
+            tf = rb["flops"] / (rb["avg_ms"] * 1e-3) / 1e12
+            extra.append({"workload": wb.name, "kernel": "bwd (pre + dkdv + dq)",
+                          "pass": "backward", "tflops": round(tf, 2),
+                          "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                          "ms_per_call": round(rb["avg_ms"], 5),
+                          "gflop": round(rb["flops"] / 1e9, 3)})
+            del wb
+            torch.cuda.empty_cache()
         for cname in sorted(gqa_inputs.CACHE_NAMED):
             wc = gqa_inputs.CACHE_NAMED[cname]()
             rec = ga.decode_num_splits(wc.batch, wc.q.shape[1], wc.k_cache.shape[2],

@@ -131,3 +131,29 @@ def test_bwd_deterministic():
     a = run_bwd(w, do)
     b = run_bwd(w, do)
     assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("which", ["bert_base_encoder", "causal_gqa_2048"])
+def test_bwd_full_size_sampled(which):
+    """The BERT-base encoder workload at full size (B 64, S 512, 12 heads,
+    d 64) and a 2048-token causal GQA shape with the Llama 3.1 8B heads
+    (32 / 8, d 128): gradients at sampled rows and keys against the sampled
+    fp64 oracle (every row's LSE and D from the full fp64 forward)."""
+    if which == "bert_base_encoder":
+        w = gqa_inputs.bert_base_encoder()
+    else:
+        w = gqa_inputs.fixed(1, 32, 8, 2048, 2048, 128, seed=33, causal=True)
+    do = _dout(w, 81)
+    dq, dk, dv = run_bwd(w, do)
+    B, S, Hq, _ = w.q.shape
+    Hkv = w.k.shape[2]
+    g = torch.Generator().manual_seed(82)
+    pick = lambda n, hi: torch.randint(0, hi, (n,), generator=g).tolist()
+    rows = list(zip(pick(24, B), pick(24, S), pick(24, Hq))) + [(0, 0, 0), (B - 1, S - 1, Hq - 1)]
+    keys = list(zip(pick(24, B), pick(24, S), pick(24, Hkv))) + [(0, 0, 0), (B - 1, S - 1, Hkv - 1)]
+    rq, rk, rv = ob.attention_grad_sampled(w.q, w.k, w.v, do, w.scale, w.causal, rows, keys)
+    got = (torch.stack([dq[b, i, h] for b, i, h in rows]),
+           torch.stack([dk[b, j, h] for b, j, h in keys]),
+           torch.stack([dv[b, j, h] for b, j, h in keys]))
+    # the scale of each tensor is the sampled reference's maximum
+    compare_grads(got, (rq, rk, rv), f"bwd full-size {which}")
