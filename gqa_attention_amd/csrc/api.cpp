@@ -12,7 +12,7 @@
 #include "validate.h"
 
 namespace gqa {
-int fwd_bf16_rows_per_tile();
+int fwd_bf16_rows_per_tile(int d);
 int fwd_f32_rows_per_tile();
 int bwd_rows_per_tile();
 }  // namespace gqa
@@ -129,7 +129,7 @@ int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *
     p.scale = scale;
     p.scale_log2 = scale * 1.4426950408889634f;
     p.num_splits = 1;
-    const int rows = dtype == GQA_DTYPE_BF16 ? gqa::fwd_bf16_rows_per_tile()
+    const int rows = dtype == GQA_DTYPE_BF16 ? gqa::fwd_bf16_rows_per_tile(d)
                                              : gqa::fwd_f32_rows_per_tile();
     p.n_rb = (int)(((long long)p.gpack * Sq + rows - 1) / rows);
     hipStream_t s = static_cast<hipStream_t>(stream);

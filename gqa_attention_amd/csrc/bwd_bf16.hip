@@ -133,7 +133,13 @@ bwd_dkdv_kernel(BwdParams p) {
     constexpr int MISC = 256;          // bytes: L and D of the tile's rows
     constexpr int SLOT = 2 * TILE * 2 + MISC;  // bytes per ring slot
     constexpr int NLOAD = 2 * NDQ + 1;         // loads per wave per tile
-    __shared__ __attribute__((aligned(1024))) unsigned char ring[NSLOT * SLOT];
+    // d = 128: the V operand lives in LDS (its 32 VGPRs would spill next to
+    // the two 64-VGPR accumulators), and a 2-slot ring keeps two workgroups
+    // per CU; d = 64: V in registers, 3-slot ring.
+    constexpr bool VLDS = D == 128;
+    constexpr int NS = VLDS ? 2 : NSLOT;
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * SLOT];
+    __shared__ __attribute__((aligned(16))) __bf16 vlds[VLDS ? NW * 32 * D : 8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -183,22 +189,25 @@ bwd_dkdv_kernel(BwdParams p) {
 
     // K and V rows of this lane's key as B operands (k = head_dim elements
     // 16 s + 8 half .. +7); keys past the end read the last key and are zeroed.
-    bf16x8 kf[DSTEPS], vf[DSTEPS];
+    bf16x8 kf[DSTEPS], vf[VLDS ? 1 : DSTEPS];
+    __bf16 *vw = vlds + (VLDS ? wave * 32 * D : 0);  // this wave's V rows (d = 128)
     {
         const int kr = key_ok ? kk : Lk - 1;
         const int64_t off = ((int64_t)(k_tok0 + kr) * p.Hkv + kvh) * D + 8 * half;
+        u32x4 x = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int s = 0; s < DSTEPS; ++s) {
             const u32x4 a = *(const u32x4 *)((const __bf16 *)p.k + off + 16 * s);
             const u32x4 c2 = *(const u32x4 *)((const __bf16 *)p.v + off + 16 * s);
             kf[s] = __builtin_bit_cast(bf16x8, key_ok ? a : u32x4{0u, 0u, 0u, 0u});
-            vf[s] = __builtin_bit_cast(bf16x8, key_ok ? c2 : u32x4{0u, 0u, 0u, 0u});
+            const u32x4 vv = key_ok ? c2 : u32x4{0u, 0u, 0u, 0u};
+            if constexpr (VLDS)  // row col, chunk 2 s + half, swizzled as the tiles
+                *(u32x4 *)(vw + col * D + (((2 * s + half) ^ swz<D>(col)) * 8)) = vv;
+            else
+                vf[s] = __builtin_bit_cast(bf16x8, vv);
+            x ^= __builtin_bit_cast(u32x4, kf[s]) ^ vv;
         }
         // Consume the loads before the first DMA (see the forward kernel).
-        u32x4 x = __builtin_bit_cast(u32x4, kf[0]) ^ __builtin_bit_cast(u32x4, vf[0]);
-#pragma unroll
-        for (int s = 1; s < DSTEPS; ++s)
-            x ^= __builtin_bit_cast(u32x4, kf[s]) ^ __builtin_bit_cast(u32x4, vf[s]);
         asm volatile("" ::"v"(x[0] ^ x[1] ^ x[2] ^ x[3]));
     }
 
@@ -220,7 +229,7 @@ bwd_dkdv_kernel(BwdParams p) {
     const float *l_src = p.ws_l + ws_base(p, b, hgl);
     const float *d_src = p.ws_d + ws_base(p, b, hgl);
     auto dma_tile = [&](int t, int slotn) {
-        unsigned char *base = ring + slotn * SLOT;
+        unsigned char *base = ring + (slotn % NS) * SLOT;
 #pragma unroll
         for (int i = 0; i < NDQ; ++i) {
             const int rho = min(t * BR + dq_row[i], rows_total - 1);
@@ -239,20 +248,18 @@ bwd_dkdv_kernel(BwdParams p) {
     // transposing read (A = X^T: in 16-lane group g, lane j reads row
     // 4 (g >> 1) + j / 4 (+ 8 for the second read) of a 16-row slot, columns
     // d0 + 4 (j % 4) .. +3 with d0 = 32 i + 16 (g & 1)).
-    int rs_rd[DSTEPS];
-#pragma unroll
-    for (int s = 0; s < DSTEPS; ++s) rs_rd[s] = col * D + (((2 * s + half) ^ swz<D>(col)) * 8);
-    // The swizzle depends on row bits 0..3, so the second read (row + 8) has
-    // its own offset; +16 and +32 rows keep the swizzle.
+    // The chunk index sits in offset bits 3.., above the 4-element half-chunk
+    // bit and below the row, so k-step s of the row-slice read is offset
+    // rs0 ^ 16 s and block i of the transposing read tr0 ^ 32 i. Rows r and
+    // r + 8 (r < 8) differ in bit 3 and swz(r + 8) = swz(r) ^ 2 for both head
+    // dims: the second transposing read is at (first ^ 16) + 8 D. The
+    // per-step offsets are formed inside the tile loop from these two bases
+    // (an XOR each) rather than held in registers.
+    const int rs0 = col * D + ((half ^ swz<D>(col)) * 8);
     const int vj = lane & 15, vg = lane >> 4;
     const int tr_row = 4 * (vg >> 1) + (vj >> 2);
-    int tr_rd[DBLK], tr_rd8[DBLK];
-#pragma unroll
-    for (int i = 0; i < DBLK; ++i) {
-        const int chunk = 4 * i + 2 * (vg & 1) + ((vj & 3) >> 1);
-        tr_rd[i] = tr_row * D + ((chunk ^ swz<D>(tr_row)) * 8) + 4 * (vj & 1);
-        tr_rd8[i] = (tr_row + 8) * D + ((chunk ^ swz<D>(tr_row + 8)) * 8) + 4 * (vj & 1);
-    }
+    const int tr0 = tr_row * D + (((2 * (vg & 1) + ((vj & 3) >> 1)) ^ swz<D>(tr_row)) * 8) +
+                    4 * (vj & 1);
 
     const float c = p.scale_log2;
     f32x16 dkacc[DBLK], dvacc[DBLK];
@@ -276,16 +283,17 @@ bwd_dkdv_kernel(BwdParams p) {
         return (t * BR) / G + shift >= wk0 + 31;
     };
 
-    if (t_lo < t_hi) {
-        dma_tile(t_lo, 0);
-        dma_tile(t_lo + 1, 1);
-    }
+    // NS - 1 tiles in flight ahead of the one being computed.
+    if (t_lo < t_hi)
+        for (int j = 0; j < NS - 1; ++j) dma_tile(t_lo + j, j);
     for (int t = t_lo; t < t_hi; ++t) {
         const int it = t - t_lo;
-        wait_barrier<NLOAD>();  // tile t has landed; every wave is done with tile t-1
-        dma_tile(t + 2, (it + 2) % NSLOT);
+        wait_barrier<(NS - 2) * NLOAD>();  // tile t has landed; every wave is done with tile t-1
+        dma_tile(t + NS - 1, it + NS - 1);
         if (!wave_needs(t)) continue;
-        const unsigned char *base = ring + (it % NSLOT) * SLOT;
+        const unsigned char *base = ring + (it % NS) * SLOT;
+        int rs_b = rs0, tr_b = tr0;
+        asm volatile("" : "+v"(rs_b), "+v"(tr_b));  // keep the derived offsets in the loop
         const __bf16 *qt = (const __bf16 *)base;
         const __bf16 *gt = (const __bf16 *)(base + TILE * 2);
         const float *misc = (const float *)(base + 2 * TILE * 2);
@@ -294,13 +302,18 @@ bwd_dkdv_kernel(BwdParams p) {
         f32x16 sacc = f32x16{}, dpacc = f32x16{};
 #pragma unroll
         for (int s = 0; s < DSTEPS; ++s) {
-            const bf16x8 a = *(const bf16x8 *)(qt + rs_rd[s]);
+            const bf16x8 a = *(const bf16x8 *)(qt + (rs_b ^ (16 * s)));
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[s], sacc, 0, 0, 0);
         }
 #pragma unroll
         for (int s = 0; s < DSTEPS; ++s) {
-            const bf16x8 a = *(const bf16x8 *)(gt + rs_rd[s]);
-            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[s], dpacc, 0, 0, 0);
+            const bf16x8 a = *(const bf16x8 *)(gt + (rs_b ^ (16 * s)));
+            bf16x8 bv;
+            if constexpr (VLDS)
+                bv = *(const bf16x8 *)(vw + (rs_b ^ (16 * s)));
+            else
+                bv = vf[s];
+            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, dpacc, 0, 0, 0);
         }
         // P = 2^(s c - L), dS = P (dP - D); masked pairs and rows past the end
         // give P = 0. B operands for k-step h2: rows 16 h2 + 8 (e/4) + 4 half + e%4.
@@ -332,7 +345,8 @@ bwd_dkdv_kernel(BwdParams p) {
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
             for (int i = 0; i < DBLK; ++i) {
-                const int o = 16 * h2 * D + tr_rd[i], o8 = 16 * h2 * D + tr_rd8[i];
+                const int tri = tr_b ^ (32 * i);
+                const int o = 16 * h2 * D + tri, o8 = 16 * h2 * D + (tri ^ 16) + 8 * D;
                 const u32x2 g0 = lds_read_tr16(gt + o), g1 = lds_read_tr16(gt + o8);
                 const u32x2 q0 = lds_read_tr16(qt + o), q1 = lds_read_tr16(qt + o8);
                 const bf16x8 ag = __builtin_bit_cast(bf16x8, u32x4{g0[0], g0[1], g1[0], g1[1]});
