@@ -113,6 +113,8 @@ fwd_bf16_kernel(FwdParams p) {
     __shared__ __attribute__((aligned(1024))) __bf16 Vs1[BN * D];
     __shared__ __attribute__((aligned(1024))) __bf16 Vs2[BN * D];
     __shared__ __attribute__((aligned(1024))) __bf16 Vs3[BN * D];
+    // The workgroup's Q rows, staged once by the same direct loads (K swizzle).
+    __shared__ __attribute__((aligned(1024))) __bf16 Qs[BM * D];
     auto kslot = [&](auto j) -> __bf16 * {
         constexpr int J = decltype(j)::value & 3;
         return J == 0 ? Ks0 : J == 1 ? Ks1 : J == 2 ? Ks2 : Ks3;
@@ -189,29 +191,12 @@ fwd_bf16_kernel(FwdParams p) {
     }
 
     // ---- Q fragment (B operand of S^T = K Q^T), kept in registers ----
+    // It arrives through LDS: its direct loads are issued just before the
+    // first K/V tiles and waited for together with them, so the workgroup's
+    // start pays one memory latency rather than the Q load's and then the
+    // first tiles'. Rows past the end are clamped to the last row (finite
+    // values whose results are never stored).
     bf16x8 qf[DSTEPS];
-    {
-        // rows past the end read the last valid row and are zeroed
-        const int qpos = row_ok ? pos : Lq - 1;
-        const int qhead = row_ok ? head : qh0;
-        const __bf16 *qrow =
-            (const __bf16 *)p.q + ((int64_t)(q_tok0 + qpos) * p.Hq + qhead) * D + 8 * half;
-#pragma unroll
-        for (int s = 0; s < DSTEPS; ++s) {
-            const u32x4 w = *(const u32x4 *)(qrow + 16 * s);
-            qf[s] = __builtin_bit_cast(bf16x8, row_ok ? w : u32x4{0u, 0u, 0u, 0u});
-        }
-    }
-
-    // Consume the Q loads before any DMA is issued: the compiler then waits for
-    // them here, instead of at their first use inside the loop, where its
-    // vmcnt wait would also drain the DMA queue.
-    {
-        u32x4 x = __builtin_bit_cast(u32x4, qf[0]);
-#pragma unroll
-        for (int s = 1; s < DSTEPS; ++s) x ^= __builtin_bit_cast(u32x4, qf[s]);
-        asm volatile("" ::"v"(x[0] ^ x[1] ^ x[2] ^ x[3]));
-    }
 
     const int64_t kv_stride = (int64_t)p.Hkv * D;
     const __bf16 *kbase = (const __bf16 *)p.k + ((int64_t)k_tok0 * p.Hkv + kvh) * D;
@@ -377,6 +362,18 @@ fwd_bf16_kernel(FwdParams p) {
     using I3 = std::integral_constant<int, 3>;
     f32x16 sa[KB], sb[KB];
     if (ntiles > 0) {
+        constexpr int NQ = BM * D * 2 / 1024 / NW;  // Q loads per wave
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int idx = 64 * (wave + NW * i) + lane;
+            const int r = idx / C8;
+            const int rho = min(row0 + r, rows_total - 1);
+            const int qp = rho / p.gpack;
+            const int qh = qh0 + (rho - qp * p.gpack);
+            const __bf16 *src = (const __bf16 *)p.q + ((int64_t)(q_tok0 + qp) * p.Hq + qh) * D +
+                                ((idx % C8) ^ CF::swz_k(r)) * 8;
+            lds_dma16(src, lds_addr(Qs) + 1024 * (wave_u + NW * i));
+        }
         dma_k(0, kslot(I0{}));
         dma_k(1, kslot(I1{}));
         dma_v(0, vslot(I0{}));
@@ -384,7 +381,10 @@ fwd_bf16_kernel(FwdParams p) {
         dma_v(1, vslot(I1{}));
         dma_k(3, kslot(I3{}));
         dma_v(2, vslot(I2{}));
-        barrier_keep2();  // K(0), K(1), V(0) have landed
+        barrier_keep2();  // Q, K(0), K(1), V(0) have landed
+        // this lane's Q row, chunk 2 s + half (same offsets as the K reads)
+#pragma unroll
+        for (int s = 0; s < DSTEPS; ++s) qf[s] = *(const bf16x8 *)(Qs + wave * 32 * D + k_rd[s]);
         if (wave_needs(0)) {
             scores(kslot(I0{}), sa);
             mask_and_max(0, sa);
