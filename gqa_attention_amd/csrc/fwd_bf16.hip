@@ -81,9 +81,12 @@ struct Waves {
 template <int D>
 struct Cfg {
     static constexpr int NW = Waves<D>::NW;
-    // keys per tile: 64 at d = 64; 32 at d = 128 keeps two score tiles, the
-    // output accumulator and the Q fragment within 256 VGPRs (2 waves/SIMD).
-    static constexpr int BN = D == 128 ? GQA_BN128 : 64;
+    // 32 keys per tile. At d = 128 this keeps two score tiles, the output
+    // accumulator and the Q fragment within 256 VGPRs (2 waves/SIMD); at
+    // d = 64 within 168 VGPRs and 48 KiB of LDS, so three workgroups share a
+    // CU (3 waves/SIMD), which measured 6-7 % faster on the encoder shape
+    // than 64-key tiles at 2 waves/SIMD.
+    static constexpr int BN = D == 128 ? GQA_BN128 : 32;
     static constexpr int C8 = D / 8;                    // 16-byte chunks per row
     static constexpr int NDMA = BN * D * 2 / 1024 / NW;  // DMA instructions per wave per tensor
     static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
@@ -93,7 +96,7 @@ struct Cfg {
 };
 
 template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(Waves<D>::NTHREADS) __attribute__((amdgpu_waves_per_eu(2))) void
+__global__ __launch_bounds__(Waves<D>::NTHREADS) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2))) void
 fwd_bf16_kernel(FwdParams p) {
     using CF = Cfg<D>;
     constexpr int NW = Waves<D>::NW, BM = Waves<D>::BM;
