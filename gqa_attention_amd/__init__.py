@@ -82,7 +82,7 @@ def lib() -> ctypes.CDLL:
     L.gqa_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                f32, i32, vp, vp, vp, sz, i32, vp]
     L.gqa_attn_bwd.restype = i32
-    L.gqa_attn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.gqa_attn_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     L.gqa_attn_bwd_workspace_bytes.restype = sz
     L.gqa_attn_decode_num_splits.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     L.gqa_attn_decode_num_splits.restype = i32
@@ -233,8 +233,8 @@ class FwdPlan:
         return self.out, self.lse
 
 
-def bwd_workspace_bytes(B: int, Hq: int, Hkv: int, Sq: int) -> int:
-    return int(lib().gqa_attn_bwd_workspace_bytes(B, Hq, Hkv, Sq))
+def bwd_workspace_bytes(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int) -> int:
+    return int(lib().gqa_attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d))
 
 
 def _prepare_bwd(q, k, v, out, lse, dout, causal, scale, cu_seqlens_q, cu_seqlens_k,
@@ -256,7 +256,7 @@ def _prepare_bwd(q, k, v, out, lse, dout, causal, scale, cu_seqlens_q, cu_seqlen
         if t.shape != ref.shape:
             raise ValueError(f"{name} must have shape {tuple(ref.shape)}")
     (qp, kp, vp_, op, lp, B, Hq, Hkv, Sq, Sk, d, sc, causal_i, cq, ck, code) = fargs
-    need = bwd_workspace_bytes(B, Hq, Hkv, Sq)
+    need = bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()

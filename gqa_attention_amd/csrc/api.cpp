@@ -51,8 +51,8 @@ int gqa_attn_decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen_k, 
     return gqa::decode_num_splits(B, Hq, Hkv, d, max_seqlen_k, window_left, ragged != 0);
 }
 
-size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq) {
-    return gqa::bwd_workspace_bytes(B, Hq, Hkv, Sq);
+size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d) {
+    return gqa::bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d);
 }
 
 int gqa_attn_bwd(const void *q, const void *k, const void *v, const void *out, const float *lse,
@@ -91,6 +91,10 @@ int gqa_attn_bwd(const void *q, const void *k, const void *v, const void *out, c
     const size_t n = gqa::bwd_workspace_floats(B, Hq, Hkv, Sq);
     p.ws_d = static_cast<float *>(workspace);
     p.ws_l = p.ws_d + n;
+    const gqa::BwdChunks ch = gqa::bwd_chunks(B, Hq, Hkv, Sq, Sk);
+    p.n_ch = ch.n_ch;
+    p.ch_tiles = ch.ch_tiles;
+    p.ws_part = p.n_ch > 1 ? p.ws_l + n : nullptr;
     (void)hipGetLastError();
     return status_from(gqa::launch_bwd_bf16(p, d, causal != 0, cu_seqlens_q != nullptr,
                                             static_cast<hipStream_t>(stream)));

@@ -120,6 +120,40 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dK, dV: a workgroup owns 128 keys of one K/V head and walks the packed rows.
 // ---------------------------------------------------------------------------
+// Sequence b's token ranges and the 32-row tiles [t_lo, t_hi) of packed rows
+// that see key block kblk (keys kblk*128 ..). Under a causal mask the first
+// such row is the first position pos with pos + (Lk - Lq) >= kblk*128.
+struct KeyBlockRows {
+    int q_tok0, Lq, k_tok0, Lk, t_lo, t_hi;
+};
+template <bool CAUSAL, bool VARLEN>
+__device__ __forceinline__ KeyBlockRows key_block_rows(const BwdParams &p, int b, int kblk) {
+    KeyBlockRows r;
+    r.q_tok0 = b * p.Sq;
+    r.Lq = p.Sq;
+    r.k_tok0 = b * p.Sk;
+    r.Lk = p.Sk;
+    if (VARLEN) {
+        r.q_tok0 = p.cu_q[b];
+        r.Lq = p.cu_q[b + 1] - r.q_tok0;
+        r.k_tok0 = p.cu_k[b];
+        r.Lk = p.cu_k[b + 1] - r.k_tok0;
+    }
+    const int rows_total = r.Lq * p.G;
+    int rho_lo = 0;
+    if (CAUSAL) rho_lo = min(rows_total, max(0, kblk * 128 - (r.Lk - r.Lq)) * p.G);
+    r.t_lo = rho_lo / 32;
+    r.t_hi = (rows_total + 31) / 32;
+    return r;
+}
+// Non-empty row chunks of a key block (at least 1: chunk 0 also covers a key
+// block that no row sees, whose gradients are zero). At most n_ch, the count
+// the workspace holds; the last chunk runs to the end of the rows.
+__device__ __forceinline__ int key_block_chunks(const BwdParams &p, const KeyBlockRows &r) {
+    if (p.n_ch <= 1) return 1;
+    return min(p.n_ch, max(1, (r.t_hi - r.t_lo + p.ch_tiles - 1) / p.ch_tiles));
+}
+
 template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2))) void
 bwd_dkdv_kernel(BwdParams p) {
@@ -146,40 +180,37 @@ bwd_dkdv_kernel(BwdParams p) {
     const int col = lane & 31, half = lane >> 5;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
-    // ---- workgroup -> (sequence, K/V head, key block) ----
+    // ---- workgroup -> (sequence, K/V head, key block, row chunk) ----
     // Key blocks of one (sequence, K/V head) run back to back on one XCD
     // when the pairs split evenly over the 8 XCDs (they share Q and dO
     // through that XCD's L2); lower key blocks (more visible rows under a
-    // causal mask) first.
+    // causal mask) first, and a key block's row chunks together.
     const int pid = blockIdx.x;
     const int n_grp = p.B * p.Hkv;
-    int grp, kblk;
+    const int n_inner = p.n_kb * p.n_ch;
+    int grp, inner;
     if ((n_grp & 7) == 0) {
         const int slot = pid >> 3;
-        grp = (slot / p.n_kb) * 8 + (pid & 7);
-        kblk = slot % p.n_kb;
+        grp = (slot / n_inner) * 8 + (pid & 7);
+        inner = slot % n_inner;
     } else {
-        grp = pid / p.n_kb;
-        kblk = pid % p.n_kb;
+        grp = pid / n_inner;
+        inner = pid % n_inner;
     }
+    const int kblk = inner / p.n_ch, chunk = inner - kblk * p.n_ch;
     const int b = grp / p.Hkv, kvh = grp - b * p.Hkv;
-    int q_tok0 = b * p.Sq, Lq = p.Sq, k_tok0 = b * p.Sk, Lk = p.Sk;
-    if (VARLEN) {
-        q_tok0 = p.cu_q[b];
-        Lq = p.cu_q[b + 1] - q_tok0;
-        k_tok0 = p.cu_k[b];
-        Lk = p.cu_k[b + 1] - k_tok0;
-    }
+    const KeyBlockRows kr = key_block_rows<CAUSAL, VARLEN>(p, b, kblk);
+    const int q_tok0 = kr.q_tok0, Lq = kr.Lq, k_tok0 = kr.k_tok0, Lk = kr.Lk;
     const int k0 = kblk * 128;
     if (k0 >= Lk) return;  // uniform over the workgroup
+    const int n_valid = key_block_chunks(p, kr);
+    if (chunk >= n_valid) return;  // uniform: an empty row chunk
     const int G = p.G;
     const int shift = Lk - Lq;
     const int rows_total = Lq * G;
-    // First packed row that sees key k0 (causal: pos + shift >= k0).
-    int rho_lo = 0;
-    if (CAUSAL) rho_lo = min(rows_total, max(0, k0 - shift) * G);
-    const int t_lo = rho_lo / BR;
-    const int t_hi = (rows_total + BR - 1) / BR;
+    // This workgroup's 32-row tiles: the key block's whole range, or one chunk.
+    const int t_lo = kr.t_lo + chunk * p.ch_tiles;
+    const int t_hi = chunk == n_valid - 1 ? kr.t_hi : t_lo + p.ch_tiles;
 
     // ---- this lane's key and this wave's key range ----
     const int kk = k0 + 32 * wave + col;
@@ -358,8 +389,27 @@ bwd_dkdv_kernel(BwdParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the (unused) tail loads
 
     // ---- write dK = scale dK^T^T and dV: lane owns key kk, head_dim
-    // elements 32 i + 8 g + 4 half .. +3 ----
+    // elements 32 i + 8 g + 4 half .. +3 (or this chunk's fp32 partials) ----
     if (!key_ok) return;
+    if (n_valid > 1) {
+        float *pk = p.ws_part + ((int64_t)(grp * p.n_kb + kblk) * p.n_ch + chunk) * (2 * 128 * D) +
+                    (32 * wave + col) * D + 4 * half;
+        float *pv = pk + 128 * D;
+#pragma unroll
+        for (int i = 0; i < DBLK; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 wk, wv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    wk[e] = dkacc[i][4 * g + e];
+                    wv[e] = dvacc[i][4 * g + e];
+                }
+                *(f32x4 *)(pk + i * 32 + 8 * g) = wk;
+                *(f32x4 *)(pv + i * 32 + 8 * g) = wv;
+            }
+        return;
+    }
     const int64_t off = ((int64_t)(k_tok0 + kk) * p.Hkv + kvh) * D + 4 * half;
     __bf16 *dkrow = (__bf16 *)p.dk + off;
     __bf16 *dvrow = (__bf16 *)p.dv + off;
@@ -376,6 +426,43 @@ bwd_dkdv_kernel(BwdParams p) {
             *(u32x2 *)(dkrow + i * 32 + 8 * g) = __builtin_bit_cast(u32x2, wk);
             *(u32x2 *)(dvrow + i * 32 + 8 * g) = __builtin_bit_cast(u32x2, wv);
         }
+}
+
+// ---------------------------------------------------------------------------
+// Sum of the row chunks' partial dK/dV for key blocks split into more than one
+// chunk, in chunk order (deterministic): one workgroup per (sequence, K/V
+// head, key block), four consecutive elements per thread and step.
+template <int D, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdParams p) {
+    const int pid = blockIdx.x;  // (b * Hkv + kvh) * n_kb + key block
+    const int grp = pid / p.n_kb, kblk = pid - grp * p.n_kb;
+    const int b = grp / p.Hkv, kvh = grp - b * p.Hkv;
+    const KeyBlockRows kr = key_block_rows<CAUSAL, VARLEN>(p, b, kblk);
+    const int k0 = kblk * 128;
+    if (k0 >= kr.Lk) return;
+    const int n_valid = key_block_chunks(p, kr);
+    if (n_valid <= 1) return;  // written directly by its only chunk
+    const float *part = p.ws_part + (int64_t)pid * p.n_ch * (2 * 128 * D);
+    constexpr int Q4 = D / 4;  // 4-element groups per key row
+    for (int idx = threadIdx.x; idx < 128 * Q4; idx += 256) {
+        const int key = idx / Q4, c4 = (idx - key * Q4) * 4;
+        if (k0 + key >= kr.Lk) continue;
+        f32x4 sk = f32x4{}, sv = f32x4{};
+        for (int c = 0; c < n_valid; ++c) {
+            const float *pc = part + (int64_t)c * (2 * 128 * D) + key * D + c4;
+            sk += *(const f32x4 *)pc;
+            sv += *(const f32x4 *)(pc + 128 * D);
+        }
+        const int64_t off = ((int64_t)(kr.k_tok0 + k0 + key) * p.Hkv + kvh) * D + c4;
+        bf16x4 wk, wv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            wk[e] = (__bf16)(sk[e] * p.scale);
+            wv[e] = (__bf16)sv[e];
+        }
+        *(u32x2 *)((__bf16 *)p.dk + off) = __builtin_bit_cast(u32x2, wk);
+        *(u32x2 *)((__bf16 *)p.dv + off) = __builtin_bit_cast(u32x2, wv);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -602,12 +689,18 @@ hipError_t launch_t(const BwdParams &p, hipStream_t s) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const long long kv_grid = (long long)p.B * p.Hkv * p.n_kb;
-    if (kv_grid > 0) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)kv_grid),
-                           dim3(NTHREADS), 0, s, p);
-        const hipError_t e = hipGetLastError();
+    const long long kv_blocks = (long long)p.B * p.Hkv * p.n_kb;
+    if (kv_blocks > 0) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN>),
+                           dim3((unsigned)(kv_blocks * p.n_ch)), dim3(NTHREADS), 0, s, p);
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (p.n_ch > 1) {
+            hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D, CAUSAL, VARLEN>),
+                               dim3((unsigned)kv_blocks), dim3(256), 0, s, p);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     const long long q_grid = (long long)p.n_hg * p.n_rb;
     if (q_grid > 0) {

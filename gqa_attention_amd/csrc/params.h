@@ -68,6 +68,14 @@ struct BwdParams {
     float scale, scale_log2;
     float *ws_d;                 // rowsum(dO * O)
     float *ws_l;                 // LSE in log2 units, +inf for rows that see no key
+    // Row chunks (n_ch = 1: none): the rows that see a key block are split
+    // into chunks of ch_tiles 32-row tiles, n_ch per key block at most (the
+    // last runs to the end). A key block with more than one non-empty chunk
+    // writes fp32 partials, [2][128 keys][d] per chunk at ws_part +
+    // (((b * Hkv + kvh) * n_kb + key block) * n_ch + chunk) * 256 d, summed
+    // into dK/dV by a reduction pass.
+    int n_ch, ch_tiles;
+    float *ws_part;
 };
 
 // Launchers (one per kernel family). Each returns a hipError_t.

@@ -92,9 +92,40 @@ inline size_t bwd_workspace_floats(int B, int Hq, int Hkv, int Sq) {
     const long long rows = (long long)B * Hkv * (((long long)Sq * G + 3) & ~3LL);
     return (size_t)(rows + kBwdPadFloats);
 }
-inline size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq) {
+// Backward row chunks. The dK/dV pass has one workgroup per (sequence, K/V
+// head, 128-key block); when there are fewer than kBwdMinBlocks of those (a
+// single sequence with few K/V heads) the rows that see each key block are
+// split into up to n_ch chunks of ch_tiles 32-row tiles (at least
+// kBwdMinChunkTiles), aiming at kBwdTargetWgs workgroups, and the chunks' fp32
+// partial dK/dV are summed afterwards. Sized for 256 CUs.
+constexpr int kBwdMinBlocks = 256, kBwdTargetWgs = 512, kBwdMinChunkTiles = 32;
+struct BwdChunks {
+    int n_ch, ch_tiles;
+};
+inline BwdChunks bwd_chunks(int B, int Hq, int Hkv, int Sq, int Sk) {
+    BwdChunks c{1, 1 << 30};
+    if (B < 1 || Hkv < 1 || Hq % Hkv != 0 || Sq < 1 || Sk < 1) return c;
+    const long long blocks = (long long)B * Hkv * ((Sk + 127) / 128);
+    if (blocks >= kBwdMinBlocks) return c;
+    const long long tiles = ((long long)Sq * (Hq / Hkv) + 31) / 32;  // most per key block
+    long long n = (kBwdTargetWgs + blocks - 1) / blocks;
+    n = n < tiles / kBwdMinChunkTiles ? n : tiles / kBwdMinChunkTiles;
+    if (n <= 1) return c;
+    c.n_ch = (int)n;
+    c.ch_tiles = (int)((tiles + n - 1) / n);
+    return c;
+}
+// Floats of partial dK/dV: per (sequence, K/V head, key block, chunk) 2 x 128 x d.
+inline size_t bwd_partial_floats(int B, int Hq, int Hkv, int Sq, int Sk, int d) {
+    const int nch = bwd_chunks(B, Hq, Hkv, Sq, Sk).n_ch;
+    if (nch <= 1) return 0;
+    const long long n_kb = (Sk + 127) / 128;
+    return (size_t)((long long)B * Hkv * n_kb * nch * 2 * 128 * d);
+}
+inline size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d) {
     const size_t n = bwd_workspace_floats(B, Hq, Hkv, Sq);
-    return n ? 2 * n * sizeof(float) : 0;
+    if (!n || Sk < 0 || (d != 64 && d != 128)) return 0;
+    return (2 * n + bwd_partial_floats(B, Hq, Hkv, Sq, Sk, d)) * sizeof(float);
 }
 
 inline int validate_bwd(const void *q, const void *k, const void *v, const void *out,
@@ -108,7 +139,7 @@ inline int validate_bwd(const void *q, const void *k, const void *v, const void 
     if (!dout || !dq || !dk || !dv) return GQA_EINVAL;
     if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
         return GQA_EINVAL;
-    if (!ws || !aligned(ws, 16) || ws_bytes < bwd_workspace_bytes(B, Hq, Hkv, Sq))
+    if (!ws || !aligned(ws, 16) || ws_bytes < bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, d))
         return GQA_EWORKSPACE;
     return GQA_OK;
 }

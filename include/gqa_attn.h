@@ -93,12 +93,15 @@ int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *
 
 /*
  * gqa_attn_bwd_workspace_bytes - size of the caller-owned workspace of
- * gqa_attn_bwd for B sequences, Hq query heads (of Hkv K/V heads) and Sq
- * query rows (the largest per-sequence length for variable length): two
- * fp32 row statistics per (sequence, head, row) plus padding. Returns 0 for
- * invalid sizes.
+ * gqa_attn_bwd for B sequences, Hq query heads (of Hkv K/V heads), Sq query
+ * and Sk key rows (the largest per-sequence lengths for variable length) and
+ * head dim d: two fp32 row statistics per (sequence, head, row) plus padding
+ * and, when B x Hkv x ceil(Sk / 128) is below 256 (too few key blocks to
+ * fill the chip, so the rows seeing each key block are split into chunks),
+ * fp32 partial key and value gradients (2 x 128 x d floats per key block and
+ * chunk). Returns 0 for invalid sizes.
  */
-size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq);
+size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int d);
 
 /*
  * gqa_attn_bwd - gradients of gqa_attn_fwd (FlashAttention-2 summary,
@@ -116,7 +119,7 @@ size_t gqa_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq);
  * with dK, dV of K/V head g summed over query heads h with h / G = g.
  * Keys that no query sees get dK = dV = 0; rows that see no key get dQ = 0.
  * workspace: device memory of at least gqa_attn_bwd_workspace_bytes(B, Hq,
- * Hkv, Sq) bytes, 16-byte aligned, contents ignored and overwritten.
+ * Hkv, Sq, Sk, d) bytes, 16-byte aligned, contents ignored and overwritten.
  * Errors: as gqa_attn_fwd, plus GQA_EWORKSPACE for a missing or short
  * workspace.
  */

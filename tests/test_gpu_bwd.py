@@ -82,6 +82,13 @@ FIXED = [
     (1, 8, 1, 1, 333, False),     # MQA, single query
     (1, 16, 2, 33, 1, False),     # single key
     (1, 32, 8, 512, 512, True),
+    # fewer than 256 (sequence, K/V head, key block) units: the rows that see
+    # each key block are split into chunks whose fp32 partial dK/dV are summed
+    # afterwards (31, 28, 10 and 14 chunks here; causal key blocks use fewer)
+    (1, 16, 1, 2100, 2100, True),
+    (1, 16, 1, 1800, 2000, True),   # Lq < Lk
+    (1, 16, 2, 1300, 1000, True),   # G = 8, Lq > Lk: early rows see no key
+    (1, 16, 1, 900, 700, False),
 ]
 
 
@@ -102,6 +109,7 @@ VARLEN = [
     ([5, 130, 0, 17], [9, 100, 3, 17], 4, 4, False),
     ([40, 130, 1], [20, 300, 7], 6, 2, True),
     ([3, 0], [0, 4], 4, 2, False),   # a sequence with no keys and one with no queries
+    ([700, 30, 1100, 0], [650, 30, 1100, 5], 16, 1, True),  # chunked and unchunked key blocks
 ]
 
 

@@ -266,8 +266,17 @@ def test_bwd_argument_errors(kw, code):
 def test_bwd_workspace_size():
     f = ga.bwd_workspace_bytes
     # two fp32 arrays of B * Hkv * round4(Sq * G) rows plus 128 spare floats each
-    assert f(2, 8, 2, 100) == 2 * 4 * (2 * 2 * 400 + 128)
-    assert f(1, 12, 12, 77) == 2 * 4 * (12 * 80 + 128)
-    assert f(0, 8, 2, 10) == 0 and f(1, 9, 2, 10) == 0 and f(1, 8, 2, -1) == 0
-    need = f(2, 8, 2, 100)
+    assert f(2, 8, 2, 100, 120, 128) == 2 * 4 * (2 * 2 * 400 + 128)
+    assert f(1, 12, 12, 77, 77, 64) == 2 * 4 * (12 * 80 + 128)
+    assert f(0, 8, 2, 10, 10, 64) == 0 and f(1, 9, 2, 10, 10, 64) == 0
+    assert f(1, 8, 2, -1, 10, 64) == 0 and f(1, 8, 2, 10, 10, 96) == 0
+    # 8 K/V heads x 64 key blocks = 512 dK/dV workgroups: no row chunks
+    assert f(1, 32, 8, 8192, 8192, 128) == 4 * 2 * (8 * 32768 + 128)
+    # MQA, one sequence: 64 key blocks (< 256) -> ceil(512 / 64) = 8 row chunks
+    # per key block, each with fp32 partial dK and dV of 128 keys x d
+    stats = 2 * (1 * 262144 + 128)
+    assert f(1, 32, 1, 8192, 8192, 128) == 4 * (stats + 1 * 64 * 8 * 2 * 128 * 128)
+    need = f(2, 8, 2, 100, 120, 128)
     assert bwd_call(ws_bytes=need - 1) == ga.GQA_EWORKSPACE
+    need = f(1, 32, 1, 8192, 8192, 128)
+    assert bwd_call(B=1, Hq=32, Hkv=1, Sq=8192, Sk=8192, ws_bytes=need - 1) == ga.GQA_EWORKSPACE
