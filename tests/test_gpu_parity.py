@@ -34,6 +34,9 @@ FIXED = [
     (1, 8, 1, 1, 333, False),     # MQA, single query
     (1, 16, 2, 33, 1, False),     # single key
     (1, 32, 8, 512, 512, True),
+    (1, 32, 1, 100, 100, True),    # MQA prefill: a row tile spans 4 (d 64) or 8 positions
+    (1, 32, 1, 77, 140, False),
+    (1, 16, 2, 1000, 1333, True),  # ragged tails on both axes, Lq < Lk
 ]
 
 
