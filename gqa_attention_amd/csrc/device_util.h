@@ -71,6 +71,15 @@ __device__ __forceinline__ void lds_dma16_u(const void *gptr, uint32_t lds_base)
                  : "s"(m), "v"(gptr)
                  : "memory", "m0");
 }
+// The same load addressed as a wave-uniform 64-bit base (scalar registers)
+// plus a 32-bit per-lane byte offset: the next tile is reached by scalar
+// arithmetic and the per-lane offsets of a full tile stay fixed.
+__device__ __forceinline__ void lds_dma16_sv(const void *sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;

@@ -208,33 +208,29 @@ fwd_bf16_kernel(FwdParams p) {
     // DMA staging: instruction i of wave w fills LDS bytes [1024 (w + NW i), +1024)
     // of a tile; lane l of it covers chunk slot (64 (w + NW i) + l) % C8 of row
     // (64 (w + NW i) + l) / C8 and fetches the global chunk that belongs there.
-    int dma_row[NDMA], dma_kc[NDMA], dma_vc[NDMA];
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-        const int idx = 64 * (wave + NW * i) + lane;
-        dma_row[i] = idx / C8;
-        dma_kc[i] = ((idx % C8) ^ CF::swz_k(dma_row[i])) * 8;
-        dma_vc[i] = ((idx % C8) ^ CF::swz_v(dma_row[i])) * 8;
-    }
-    // Rows past kend are clamped to the last needed key: they are real, finite
-    // K/V rows, their scores are masked to -inf and their p is exactly 0.
+    // A tile is addressed as a wave-uniform base (scalar arithmetic) plus a
+    // 32-bit per-lane byte offset. Rows past kend are clamped to the last
+    // needed key, and steps past the last needed tile (issued so that every
+    // step has the same number of loads) re-load it: real, finite K/V rows
+    // whose scores are masked to -inf or never used.
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    auto dma_k = [&](int t, __bf16 *dst) {
+    auto dma_kv = [&](const __bf16 *base, int t, auto is_v, __bf16 *dst) {
+        const int tt = min(t, ntiles - 1);  // a tile holding needed keys
+        const int rows = kend - tt * BN;    // its needed rows (>= 1)
+        const __bf16 *tile = base + (int64_t)tt * BN * kv_stride;
+        const uint32_t lds0 = lds_addr(dst) + 1024 * wave_u;
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) {
-            const __bf16 *src =
-                kbase + (int64_t)min(t * BN + dma_row[i], kend - 1) * kv_stride + dma_kc[i];
-            lds_dma16(src, lds_addr(dst) + 1024 * (wave_u + NW * i));
+            const int idx = 64 * (wave_u + NW * i) + lane;
+            const int r = idx / C8;
+            const int sw = decltype(is_v)::value ? CF::swz_v(r) : CF::swz_k(r);
+            const int ch = ((idx % C8) ^ sw) * 8;
+            lds_dma16_sv(tile, (uint32_t)((min(r, rows - 1) * kv_stride + ch) * 2),
+                         lds0 + 1024 * NW * i);
         }
     };
-    auto dma_v = [&](int t, __bf16 *dst) {
-#pragma unroll
-        for (int i = 0; i < NDMA; ++i) {
-            const __bf16 *src =
-                vbase + (int64_t)min(t * BN + dma_row[i], kend - 1) * kv_stride + dma_vc[i];
-            lds_dma16(src, lds_addr(dst) + 1024 * (wave_u + NW * i));
-        }
-    };
+    auto dma_k = [&](int t, __bf16 *dst) { dma_kv(kbase, t, std::false_type{}, dst); };
+    auto dma_v = [&](int t, __bf16 *dst) { dma_kv(vbase, t, std::true_type{}, dst); };
     // Barrier that lets the two most recent DMA groups (2 x 2 NDMA loads per
     // wave) stay in flight: everything older has landed in LDS for this wave,
     // and after s_barrier for every wave. No release fence (which would drain
