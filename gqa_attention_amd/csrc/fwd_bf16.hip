@@ -128,7 +128,9 @@ fwd_bf16_kernel(FwdParams p) {
     };
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    // the wave index is wave-uniform: kept in a scalar register so that the
+    // per-wave conditions below are scalar branches, not lane masks
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, half = lane >> 5;
 
     // ---- workgroup -> (head group, row tile) ----
@@ -183,15 +185,13 @@ fwd_bf16_kernel(FwdParams p) {
     const int head = qh0 + (rho - pos * p.gpack);
     const int row_kend = CAUSAL ? min(Lk, pos + 1 + shift) : Lk;
 
-    // ---- this wave's row range: which tiles it needs and which need masking ----
-    const int wr0 = row0 + wave * 32;
-    const bool wave_live = wr0 < rows_total;
-    const int wr1 = min(wr0 + 31, rows_total - 1);
-    int wave_kend = Lk, wave_kfull = Lk;
-    if (CAUSAL) {
-        wave_kend = min(Lk, wr1 / p.gpack + 1 + shift);
-        wave_kfull = min(Lk, wr0 / p.gpack + 1 + shift);
-    }
+    // ---- this wave's rows: from which key on its tiles need masking ----
+    // Every wave runs every tile of the workgroup (one path, no per-wave
+    // branches in the loop). A tile that lies wholly past a wave's causal
+    // limit is masked to -inf, so it adds nothing: p = 0 and no max moves.
+    // Rows past the end hold clamped copies of the last row and are never
+    // stored.
+    const int wave_kfull = CAUSAL ? min(Lk, (row0 + wave * 32) / p.gpack + 1 + shift) : Lk;
 
     // ---- Q fragment (B operand of S^T = K Q^T), kept in registers ----
     // It arrives through LDS: its direct loads are issued just before the
@@ -213,19 +213,20 @@ fwd_bf16_kernel(FwdParams p) {
     // needed key, and steps past the last needed tile (issued so that every
     // step has the same number of loads) re-load it: real, finite K/V rows
     // whose scores are masked to -inf or never used.
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t row_bytes = (uint32_t)kv_stride * 2;  // < 2^24 (Hkv d <= 2^22)
+    const uint32_t tile_bytes = BN * row_bytes;
     auto dma_kv = [&](const __bf16 *base, int t, auto is_v, __bf16 *dst) {
-        const int tt = min(t, ntiles - 1);  // a tile holding needed keys
-        const int rows = kend - tt * BN;    // its needed rows (>= 1)
-        const __bf16 *tile = base + (int64_t)tt * BN * kv_stride;
-        const uint32_t lds0 = lds_addr(dst) + 1024 * wave_u;
+        const int tt = min(t, ntiles - 1);   // a tile holding needed keys
+        const int last = kend - 1 - tt * BN;  // its last needed row (>= 0)
+        const char *tile = (const char *)base + (uint64_t)(uint32_t)tt * tile_bytes;
+        const uint32_t lds0 = lds_addr(dst) + 1024 * wave;
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) {
-            const int idx = 64 * (wave_u + NW * i) + lane;
+            const int idx = 64 * (wave + NW * i) + lane;
             const int r = idx / C8;
             const int sw = decltype(is_v)::value ? CF::swz_v(r) : CF::swz_k(r);
-            const int ch = ((idx % C8) ^ sw) * 8;
-            lds_dma16_sv(tile, (uint32_t)((min(r, rows - 1) * kv_stride + ch) * 2),
+            const uint32_t ch_bytes = ((idx % C8) ^ sw) * 16;
+            lds_dma16_sv(tile, __umul24((uint32_t)min(r, last), row_bytes) + ch_bytes,
                          lds0 + 1024 * NW * i);
         }
     };
@@ -280,10 +281,11 @@ fwd_bf16_kernel(FwdParams p) {
             }
         }
     };
-    // Element mask (only on tiles crossing the diagonal or the end), then the
-    // tile's row max and the reference-max update with the rare rescale of O~.
+    // Element mask (only on tiles crossing the diagonal or the end, and on the
+    // tile past the end whose scores the last step computes), then the tile's
+    // row max and the reference-max update with the rare rescale of O~.
     auto mask_and_max = [&](int t, f32x16 (&sacc)[KB]) {
-        if ((t + 1) * BN > wave_kfull) {
+        if ((t + 1) * BN > wave_kfull || t >= ntiles) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -343,7 +345,6 @@ fwd_bf16_kernel(FwdParams p) {
                     oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][h2], oacc[i], 0, 0, 0);
                 }
     };
-    auto wave_needs = [&](int t) { return wave_live && t < ntiles && t * BN < wave_kend; };
 
     // Software pipeline, one barrier per tile, DMA three tiles ahead.
     // Entering step t: K(t+1) and V(t) have landed in LDS, the DMA of K(t+2),
@@ -352,9 +353,10 @@ fwd_bf16_kernel(FwdParams p) {
     // (into K(t)'s slot) and V(t+3) (into V(t-1)'s slot), computes the scores
     // of tile t+1 on the matrix cores while the vector units turn tile t into
     // probabilities, accumulates P(t) V(t), then waits until K(t+2) and
-    // V(t+1) have landed and meets the other waves. Tiles past the end are
-    // loaded from the clamped last row (never used) so that every step issues
-    // the same number of DMA loads and the wait count stays exact.
+    // V(t+1) have landed and meets the other waves. Steps past the last
+    // needed tile re-load that tile (never used) so that every step issues the
+    // same number of DMA loads and the wait count stays exact; the last step
+    // also scores K(ntiles), such a re-load, and masks all of it.
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
@@ -371,7 +373,7 @@ fwd_bf16_kernel(FwdParams p) {
             const int qh = qh0 + (rho - qp * p.gpack);
             const __bf16 *src = (const __bf16 *)p.q + ((int64_t)(q_tok0 + qp) * p.Hq + qh) * D +
                                 ((idx % C8) ^ CF::swz_k(r)) * 8;
-            lds_dma16(src, lds_addr(Qs) + 1024 * (wave_u + NW * i));
+            lds_dma16(src, lds_addr(Qs) + 1024 * (wave + NW * i));
         }
         dma_k(0, kslot(I0{}));
         dma_k(1, kslot(I1{}));
@@ -384,10 +386,8 @@ fwd_bf16_kernel(FwdParams p) {
         // this lane's Q row, chunk 2 s + half (same offsets as the K reads)
 #pragma unroll
         for (int s = 0; s < DSTEPS; ++s) qf[s] = *(const bf16x8 *)(Qs + wave * 32 * D + k_rd[s]);
-        if (wave_needs(0)) {
-            scores(kslot(I0{}), sa);
-            mask_and_max(0, sa);
-        }
+        scores(kslot(I0{}), sa);
+        mask_and_max(0, sa);
         barrier_lds();  // K(0)'s slot is refilled with K(4) in step 0
     }
 
@@ -395,11 +395,10 @@ fwd_bf16_kernel(FwdParams p) {
         constexpr int J = decltype(jc)::value;
         __bf16 *k_next = kslot(std::integral_constant<int, J + 1>{});  // K(t+1)
         __bf16 *v_cur = vslot(std::integral_constant<int, J>{});       // V(t)
-        const bool do_t = wave_needs(t), do_n = wave_needs(t + 1);
         dma_k(t + 4, kslot(std::integral_constant<int, J>{}));
         dma_v(t + 3, vslot(std::integral_constant<int, J + 3>{}));
         bf16x8 pf[KB][2];
-        if (do_t && do_n) {
+        {
             scores(k_next, s_nxt);
             probs(s_cur, pf);
             accumulate(v_cur, pf);
@@ -426,14 +425,8 @@ fwd_bf16_kernel(FwdParams p) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (P.V)
                 __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
             }
-        } else {
-            if (do_n) scores(k_next, s_nxt);
-            if (do_t) {
-                probs(s_cur, pf);
-                accumulate(v_cur, pf);
-            }
         }
-        if (do_n) mask_and_max(t + 1, s_nxt);
+        mask_and_max(t + 1, s_nxt);
         barrier_keep2();
     };
     int t = 0;

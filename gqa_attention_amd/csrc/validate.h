@@ -44,6 +44,9 @@ inline int validate_fwd(const void *q, const void *k, const void *v, const void 
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
         !aligned(lse, 4))
         return GQA_EINVAL;
+    // K/V row pitch: the forward kernel addresses a key tile with 24-bit
+    // per-lane byte offsets (row pitch 2 Hkv d bytes < 2^24).
+    if ((long long)Hkv * d > (1LL << 22)) return GQA_EINVAL;
     // Launch grid: head groups x row tiles must fit a 1-D grid (<= 2^31 - 1).
     const long long tiles = ((long long)Hq * Sq + 31) / 32;
     if ((long long)B * tiles > 0x7fffffffLL) return GQA_EINVAL;

@@ -84,7 +84,8 @@ enum {
  * causal != 0 masks key j for query row i when j > i + (Lk - Lq) (per
  * sequence; the diagonal is kept; bottom-right alignment when Lq != Lk).
  * Requirements: B, Hq, Hkv >= 1; Sq, Sk >= 1 for fixed length and >= 0 for
- * variable length; Hq % Hkv == 0.
+ * variable length; Hq % Hkv == 0; Hkv * d <= 4194304 (one token's K row at
+ * most 8 MiB, so per-lane offsets inside a key tile fit 24 bits).
  */
 int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
                  int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,

@@ -95,6 +95,7 @@ FWD_ERRORS = [
     (dict(out=FAKE + 4), ga.GQA_EINVAL),
     (dict(lse=FAKE + 2), ga.GQA_EINVAL),
     (dict(cu_q=FAKE + 2, cu_k=FAKE), ga.GQA_EINVAL),
+    (dict(Hq=65536, Hkv=65536, d=128), ga.GQA_EINVAL),  # K/V row pitch >= 2^24 bytes
 ]
 
 
