@@ -19,6 +19,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Largest amount (log2 units) by which a tile's row max may exceed the running
 // reference max before the unnormalised output is rescaled (p <= 2^8 = 256).
 constexpr float kRescaleGap = 8.0f;
+// Largest sum of one lane's probabilities over a forward tile (16 values)
+// before the tile is recomputed against a raised reference max; every p of an
+// accepted tile is then <= 2^12.
+constexpr float kTileSumBound = 4096.0f;
 
 // Combine a value with the one held by lane (l ^ 32). v_permlane32_swap
 // exchanges the two 32-lane halves, so (r[0], r[1]) hold the pair

@@ -57,9 +57,6 @@ namespace {
 #ifndef GQA_VR_DIV
 #define GQA_VR_DIV 1
 #endif
-#ifndef GQA_PV_RD
-#define GQA_PV_RD 0
-#endif
 
 // Wavefronts per workgroup (32 query rows each): 8 at d = 128, where sharing
 // each K/V tile among 256 rows measured 3-5 % faster than 128 rows, 4 at
@@ -281,10 +278,9 @@ fwd_bf16_kernel(FwdParams p) {
             }
         }
     };
-    // Element mask (only on tiles crossing the diagonal or the end, and on the
-    // tile past the end whose scores the last step computes), then the tile's
-    // row max and the reference-max update with the rare rescale of O~.
-    auto mask_and_max = [&](int t, f32x16 (&sacc)[KB]) {
+    // Element mask, only on tiles crossing the diagonal or the end, and on the
+    // tile past the end whose scores the last step computes.
+    auto mask = [&](int t, f32x16 (&sacc)[KB]) {
         if ((t + 1) * BN > wave_kfull || t >= ntiles) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -294,18 +290,17 @@ fwd_bf16_kernel(FwdParams p) {
                     if (key >= row_kend) sacc[kb][r] = -INFINITY;
                 }
         }
+    };
+    // Move the reference max m up to the tile's row max (when that is larger)
+    // and rescale O~ and l by 2^(m_old - m_new).
+    auto raise_max = [&](const f32x16 (&sacc)[KB]) {
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-        mx = pair_max32(mx);
-        // The reference max only moves when the tile max exceeds it by more
-        // than kRescaleGap (log2 units); every p then stays <= 2^kRescaleGap
-        // and the rescale of O~ is skipped on almost every tile. The result
-        // is the same: m cancels between O~ and l and is added back in L.
-        const float mxs = mx * c;
-        if (mxs > m_run + kRescaleGap) {
+        const float mxs = pair_max32(mx) * c;
+        if (mxs > m_run) {
             const float alpha = fast_exp2(m_run - mxs);
             m_run = mxs;
             l_run *= alpha;
@@ -315,9 +310,11 @@ fwd_bf16_kernel(FwdParams p) {
                 for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
         }
     };
-    // p = 2^(s c - m) in fp32 (summed into l), rounded to bf16 as the B operand.
-    auto probs = [&](const f32x16 (&sacc)[KB], bf16x8 (&pf)[KB][2]) {
+    // p = 2^(s c - m) in fp32, summed into l_tile and rounded to bf16 as the B
+    // operand.
+    auto probs = [&](const f32x16 (&sacc)[KB], bf16x8 (&pf)[KB][2], float &l_tile) {
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        l_tile = 0.f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -325,13 +322,13 @@ fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const float pv = fast_exp2(fmaf(sacc[kb][8 * h2 + j], c, -m_use));
-                    l_run += pv;
+                    l_tile += pv;
                     pf[kb][h2][j] = (__bf16)pv;
                 }
     };
     // O^T += V^T P^T. P^T key order in lane (col, half) for k-slot j:
     // key = kb*32 + 16*h2 + 8*(j/4) + 4*half + j%4, matched by the V^T reads.
-    auto accumulate = [&](const __bf16 *vs, const bf16x8 (&pf)[KB][2]) {
+    auto load_v = [&](const __bf16 *vs, bf16x8 (&vf)[KB][2][DBLK]) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -341,19 +338,28 @@ fwd_bf16_kernel(FwdParams p) {
                     const __bf16 *vp = vs + (kb * 32 + 16 * h2) * D + v_rd[i];
                     const u32x2 lo = lds_read_tr16(vp);
                     const u32x2 hi = lds_read_tr16(vp + 8 * D);
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-                    oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][h2], oacc[i], 0, 0, 0);
+                    vf[kb][h2][i] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
                 }
+    };
+    auto accumulate = [&](const bf16x8 (&vf)[KB][2][DBLK], const bf16x8 (&pf)[KB][2]) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < DBLK; ++i)
+                    oacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kb][h2][i], pf[kb][h2],
+                                                                     oacc[i], 0, 0, 0);
     };
 
     // Software pipeline, one barrier per tile, DMA three tiles ahead.
     // Entering step t: K(t+1) and V(t) have landed in LDS, the DMA of K(t+2),
     // K(t+3), V(t+1), V(t+2) may be in flight, and the scores of tile t are
-    // masked with the reference max updated. Step t starts the DMA of K(t+4)
-    // (into K(t)'s slot) and V(t+3) (into V(t-1)'s slot), computes the scores
-    // of tile t+1 on the matrix cores while the vector units turn tile t into
-    // probabilities, accumulates P(t) V(t), then waits until K(t+2) and
-    // V(t+1) have landed and meets the other waves. Steps past the last
+    // masked. Step t starts the DMA of K(t+4) (into K(t)'s slot) and V(t+3)
+    // (into V(t-1)'s slot), computes the scores of tile t+1 on the matrix
+    // cores while the vector units turn tile t into probabilities (checked
+    // against the reference max), accumulates P(t) V(t), masks tile t+1, then
+    // waits until K(t+2) and V(t+1) have landed and meets the other waves. Steps past the last
     // needed tile re-load that tile (never used) so that every step issues the
     // same number of DMA loads and the wait count stays exact; the last step
     // also scores K(ntiles), such a re-load, and masks all of it.
@@ -387,7 +393,8 @@ fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int s = 0; s < DSTEPS; ++s) qf[s] = *(const bf16x8 *)(Qs + wave * 32 * D + k_rd[s]);
         scores(kslot(I0{}), sa);
-        mask_and_max(0, sa);
+        mask(0, sa);
+        raise_max(sa);
         barrier_lds();  // K(0)'s slot is refilled with K(4) in step 0
     }
 
@@ -398,20 +405,18 @@ fwd_bf16_kernel(FwdParams p) {
         dma_k(t + 4, kslot(std::integral_constant<int, J>{}));
         dma_v(t + 3, vslot(std::integral_constant<int, J + 3>{}));
         bf16x8 pf[KB][2];
+        bf16x8 vf[KB][2][DBLK];
+        float l_tile;
         {
+            // The scores of tile t+1 run on the matrix cores while the vector
+            // units turn tile t into probabilities: each score MFMA is followed
+            // by a slice of the exponentials and of the LDS reads.
             scores(k_next, s_nxt);
-            probs(s_cur, pf);
-            accumulate(v_cur, pf);
-            // Interleave: each score MFMA of tile t+1 is followed by a slice of
-            // tile t's exponentials and the LDS reads for the next products,
-            // so the vector units work while the matrix cores run.
+            load_v(v_cur, vf);
+            probs(s_cur, pf, l_tile);
             constexpr int NSM = KB * DSTEPS;    // score MFMAs
-            constexpr int NPM = KB * 2 * DBLK;  // P.V MFMAs
-            constexpr int NVR = 2 * NPM;        // transposing V reads
+            constexpr int NVR = 2 * KB * 2 * DBLK;  // transposing V reads
             constexpr int VALU_PER = (KB * 16 * 7 / 2 + NSM - 1) / NSM;
-            // LDS operand reads run GQA_PF_K score-MFMAs ahead of their use;
-            // V reads are spread over the score phase so that the P.V MFMAs
-            // find their operands in registers.
             __builtin_amdgcn_sched_group_barrier(0x100, GQA_PF_K, 0);
 #pragma unroll
             for (int g = 0; g < NSM; ++g) {
@@ -419,14 +424,21 @@ fwd_bf16_kernel(FwdParams p) {
                 __builtin_amdgcn_sched_group_barrier(0x100, 1 + NVR / NSM / GQA_VR_DIV, 0);  // DS reads
                 __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER, 0);  // VALU (exp)
             }
-#pragma unroll
-            for (int g = 0; g < NPM; ++g) {
-                __builtin_amdgcn_sched_group_barrier(0x100, GQA_PV_RD, 0);  // DS reads (V)
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (P.V)
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
-            }
         }
-        mask_and_max(t + 1, s_nxt);
+        // The reference m of a row is its exact max over tile 0 (every row that
+        // sees any key sees key 0) and then moves only when a tile's
+        // probabilities grow large: when some lane's sum over the tile exceeds
+        // kTileSumBound (so one p may exceed it), the wave raises m to the tile
+        // max, rescales O~ and l, and recomputes the tile. Otherwise every
+        // p <= kTileSumBound and no row max is computed. The result is the same
+        // for any reference: m cancels between O~ and l and is added back in L.
+        if (__builtin_amdgcn_ballot_w64(l_tile > kTileSumBound)) {
+            raise_max(s_cur);
+            probs(s_cur, pf, l_tile);
+        }
+        l_run += l_tile;
+        accumulate(vf, pf);
+        mask(t + 1, s_nxt);
         barrier_keep2();
     };
     int t = 0;

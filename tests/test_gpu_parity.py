@@ -53,6 +53,43 @@ def test_fixed(shape, d, dtype):
     compare(o, l, ro, rl, dtype, f"fixed {shape} d={d}")
 
 
+def _scaled_keys(w, profile):
+    """The same workload with each key row scaled by profile[j] (then rounded
+    to the input dtype again), so that score magnitudes change along the keys."""
+    f = torch.tensor(profile, dtype=torch.float32).view(1, -1, 1, 1)
+    w.k = (w.k.float() * f).to(w.k.dtype)
+    return w
+
+
+KEY_PROFILES = {
+    # later tiles reach scores tens of log2 units above every score of tile 0,
+    # so the reference max must move many times
+    "growing": lambda sk: [0.1 + 6.0 * j / sk for j in range(sk)],
+    # the first tile holds the largest scores; later tiles underflow
+    "shrinking": lambda sk: [6.0 - 5.9 * j / sk for j in range(sk)],
+    # one key per 97 has scores 12x larger than the rest (spikes in any tile)
+    "spikes": lambda sk: [12.0 if j % 97 == 41 else 1.0 for j in range(sk)],
+}
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("profile", sorted(KEY_PROFILES))
+def test_score_range_along_keys(profile, causal, d):
+    """Scores whose range moves along the key axis (bf16): the running
+    reference of the streaming softmax is raised, or never raised, many times
+    over a row, and the result still matches the oracle. (fp32 mode is left
+    out: scores here reach about 50 in magnitude, and rounding s to fp32
+    alone moves p by up to 50 x 2^-24 relative, above its 1e-5 bound.)"""
+    dtype = torch.bfloat16
+    w = gqa_inputs.fixed(2, 8, 2, 300, 700, d, seed=5000 + d + 7 * causal, dtype=dtype,
+                         causal=causal)
+    w = _scaled_keys(w, KEY_PROFILES[profile](700))
+    o, l = run_fwd(w)
+    ro, rl = oracle_fwd(w)
+    compare(o, l, ro, rl, dtype, f"{profile} causal={causal} d={d}")
+
+
 VARLEN = [
     # lengths_q, lengths_k, Hq, Hkv, causal
     ([0, 1, 63, 64, 65, 200], [0, 1, 63, 64, 65, 200], 8, 2, True),
