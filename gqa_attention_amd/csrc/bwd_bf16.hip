@@ -176,9 +176,11 @@ bwd_dkdv_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) __bf16 vlds[VLDS ? NW * 32 * D : 8];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    // wave-uniform wave index (scalar register): per-wave conditions are
+    // scalar branches
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, half = lane >> 5;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int wave_u = wave;
 
     // ---- workgroup -> (sequence, K/V head, key block, row chunk) ----
     // Key blocks of one (sequence, K/V head) run back to back on one XCD
@@ -215,6 +217,9 @@ bwd_dkdv_kernel(BwdParams p) {
     // ---- this lane's key and this wave's key range ----
     const int kk = k0 + 32 * wave + col;
     const bool key_ok = kk < Lk;
+    // causal: packed row rho sees key kk iff rho / G + shift >= kk, i.e.
+    // rho >= (kk - shift) G
+    const int row_min = (kk - shift) * G;
     const int wk0 = k0 + 32 * wave;             // first key of this wave
     const int wk1 = min(wk0 + 31, Lk - 1);      // last valid key of this wave
 
@@ -300,18 +305,14 @@ bwd_dkdv_kernel(BwdParams p) {
         dvacc[i] = f32x16{};
     }
 
-    // Does this wave's key range meet tile t? Is every (row, key) pair of the
-    // tile visible (no element mask needed)?
-    auto wave_needs = [&](int t) {
-        if (wk0 >= Lk) return false;
-        if (!CAUSAL) return true;
-        const int last_row = min(t * BR + BR, rows_total) - 1;
-        return last_row / G + shift >= wk0;
-    };
+    // Does every row of tile t exist and see every key of this wave (no
+    // element mask needed)? Keys past the end are not masked: a lane's key
+    // only reaches its own column of dK^T and dV^T, and the columns of keys
+    // past the end are never stored.
     auto tile_full = [&](int t) {
-        if (t * BR + BR > rows_total || wk1 < wk0 + 31) return false;
+        if (t * BR + BR > rows_total) return false;
         if (!CAUSAL) return true;
-        return (t * BR) / G + shift >= wk0 + 31;
+        return (t * BR) / G + shift >= wk1;
     };
 
     // NS - 1 tiles in flight ahead of the one being computed.
@@ -321,7 +322,9 @@ bwd_dkdv_kernel(BwdParams p) {
         const int it = t - t_lo;
         wait_barrier<(NS - 2) * NLOAD>();  // tile t has landed; every wave is done with tile t-1
         dma_tile(t + NS - 1, it + NS - 1);
-        if (!wave_needs(t)) continue;
+        // Every wave runs every tile of the range (one path, no per-wave
+        // skip): under a causal mask a tile wholly above this wave's keys
+        // is masked to P = dS = 0.
         const unsigned char *base = ring + (it % NS) * SLOT;
         int rs_b = rs0, tr_b = tr0;
         asm volatile("" : "+v"(rs_b), "+v"(tr_b));  // keep the derived offsets in the loop
@@ -348,8 +351,7 @@ bwd_dkdv_kernel(BwdParams p) {
         }
         // P = 2^(s c - L), dS = P (dP - D); masked pairs and rows past the end
         // give P = 0. B operands for k-step h2: rows 16 h2 + 8 (e/4) + 4 half + e%4.
-        const bool full = tile_full(t);
-        bf16x8 pf[2], dsf[2];
+        float pv[16], dsv[16];
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
             const f32x4 lv = *(const f32x4 *)(misc + 16 * blk + 4 * half);
@@ -357,19 +359,26 @@ bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int j = 4 * blk + e;
-                float pv = fast_exp2(fmaf(sacc[j], c, -lv[e]));
-                float ds = pv * (dpacc[j] - dv4[e]);
-                if (!full) {
-                    // rows past the end carry arbitrary L and D: select, not scale
-                    const int rho = t * BR + 8 * blk + 4 * half + e;
-                    const bool vis = rho < rows_total && key_ok &&
-                                     (!CAUSAL || kk <= rho / G + shift);
-                    pv = vis ? pv : 0.f;
-                    ds = vis ? ds : 0.f;
-                }
-                pf[blk >> 1][4 * (blk & 1) + e] = (__bf16)pv;
-                dsf[blk >> 1][4 * (blk & 1) + e] = (__bf16)ds;
+                pv[j] = fast_exp2(fmaf(sacc[j], c, -lv[e]));
+                dsv[j] = pv[j] * (dpacc[j] - dv4[e]);
             }
+        }
+        if (!tile_full(t)) {
+            // rows past the end carry arbitrary L and D: select, not scale
+            const int rho0 = t * BR + 4 * half;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int rho = rho0 + 8 * (j >> 2) + (j & 3);
+                const bool vis = rho < rows_total && (!CAUSAL || rho >= row_min);
+                pv[j] = vis ? pv[j] : 0.f;
+                dsv[j] = vis ? dsv[j] : 0.f;
+            }
+        }
+        bf16x8 pf[2], dsf[2];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            pf[j >> 3][j & 7] = (__bf16)pv[j];
+            dsf[j >> 3][j & 7] = (__bf16)dsv[j];
         }
         // dV^T += dO^T P, dK^T += Q^T dS (A operands by transposing reads).
 #pragma unroll
