@@ -264,16 +264,35 @@ bwd_dkdv_kernel(BwdParams p) {
     const int qh0 = hgl * G;
     const float *l_src = p.ws_l + ws_base(p, b, hgl);
     const float *d_src = p.ws_d + ws_base(p, b, hgl);
+    // Tiles are fetched in order (t_lo, t_lo + 1, ...), so each lane keeps its
+    // next row as (position, head in group) and steps it by BR rows per tile
+    // instead of dividing by G every time.
+    const int step_pos = BR / G, step_hd = BR - step_pos * G;
+    int dpos[NDQ], dhd[NDQ];
+#pragma unroll
+    for (int i = 0; i < NDQ; ++i) {
+        const int rho = t_lo * BR + dq_row[i];
+        dpos[i] = rho / G;
+        dhd[i] = rho - dpos[i] * G;
+    }
     auto dma_tile = [&](int t, int slotn) {
+        (void)t;  // the lanes' row state holds tile t
         unsigned char *base = ring + (slotn % NS) * SLOT;
 #pragma unroll
         for (int i = 0; i < NDQ; ++i) {
-            const int rho = min(t * BR + dq_row[i], rows_total - 1);
-            const int pos = rho / G;
-            const int64_t off = ((int64_t)(q_tok0 + pos) * p.Hq + qh0 + (rho - pos * G)) * D + dq_c[i];
+            // rows past the end read the last row
+            const bool in = dpos[i] < Lq;
+            const int pos = in ? dpos[i] : Lq - 1, hd = in ? dhd[i] : G - 1;
+            const int64_t off = ((int64_t)(q_tok0 + pos) * p.Hq + qh0 + hd) * D + dq_c[i];
             const uint32_t dst = lds_addr(base) + 1024 * (wave_u + NW * i);
             lds_dma16_u((const __bf16 *)p.q + off, dst);
             lds_dma16_u((const __bf16 *)p.dout + off, dst + TILE * 2);
+            dhd[i] += step_hd;
+            dpos[i] += step_pos;
+            if (dhd[i] >= G) {
+                dhd[i] -= G;
+                ++dpos[i];
+            }
         }
         const int r8 = t * BR + 8 * wave + 4 * (lane & 1);
         const float *src = (lane & 2) ? d_src + r8 : l_src + r8;
