@@ -512,9 +512,9 @@ bwd_dq_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) __bf16 ring[NSLOT * 2 * TILE];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    // wave-uniform wave index (scalar register)
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, half = lane >> 5;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
     // ---- workgroup -> (head group, row tile), as the forward ----
     const int pid = blockIdx.x;
@@ -554,14 +554,10 @@ bwd_dq_kernel(BwdParams p) {
     const int pos = rho / G;
     const int head = qh0 + (rho - pos * G);
     const int row_kend = CAUSAL ? min(Lk, pos + 1 + shift) : Lk;
-    const int wr0 = row0 + wave * 32;
-    const bool wave_live = wr0 < rows_total;
-    const int wr1 = min(wr0 + 31, rows_total - 1);
-    int wave_kend = Lk, wave_kfull = Lk;
-    if (CAUSAL) {
-        wave_kend = min(Lk, wr1 / G + 1 + shift);
-        wave_kfull = min(Lk, wr0 / G + 1 + shift);
-    }
+    // Every wave runs every key tile of the workgroup (one path, no per-wave
+    // skip); keys past a row's causal limit are masked to P = 0, and rows
+    // past the end have L = +inf (P = 0) and are never stored.
+    const int wave_kfull = CAUSAL ? min(Lk, (row0 + wave * 32) / G + 1 + shift) : Lk;
 
     // Per-row statistics and the Q^T / dO^T fragments (B operands).
     float lrow = INFINITY, drow = 0.f;
@@ -599,17 +595,26 @@ bwd_dq_kernel(BwdParams p) {
         dk_row[i] = idx / C8;
         dk_c[i] = ((idx % C8) ^ swz<D>(dk_row[i])) * 8;
     }
+    // A key tile is addressed as a wave-uniform base (scalar registers) plus
+    // 24-bit per-lane byte offsets; rows past kend read the last needed key
+    // and tiles past the end re-load the last needed tile.
     const int64_t kv_stride = (int64_t)p.Hkv * D;
-    const __bf16 *kbase = (const __bf16 *)p.k + ((int64_t)k_tok0 * p.Hkv + kvh) * D;
-    const __bf16 *vbase = (const __bf16 *)p.v + ((int64_t)k_tok0 * p.Hkv + kvh) * D;
+    const char *kbase = (const char *)((const __bf16 *)p.k + ((int64_t)k_tok0 * p.Hkv + kvh) * D);
+    const char *vbase = (const char *)((const __bf16 *)p.v + ((int64_t)k_tok0 * p.Hkv + kvh) * D);
+    const uint32_t row_bytes = (uint32_t)kv_stride * 2;  // < 2^24 (Hkv d <= 2^22)
+    const uint32_t tile_bytes = BN * row_bytes;
     auto dma_tile = [&](int t, int slotn) {
         __bf16 *kd = ring + slotn * 2 * TILE;
+        const int tt = min(t, ntiles - 1);
+        const int last = kend - 1 - tt * BN;  // last needed row of the tile (>= 0)
+        const uint64_t toff = (uint64_t)(uint32_t)tt * tile_bytes;
 #pragma unroll
         for (int i = 0; i < NDK; ++i) {
-            const int64_t roff = (int64_t)min(t * BN + dk_row[i], kend - 1) * kv_stride + dk_c[i];
-            const uint32_t dst = lds_addr(kd) + 1024 * (wave_u + NW * i);
-            lds_dma16_u(kbase + roff, dst);
-            lds_dma16_u(vbase + roff, dst + TILE * 2);
+            const uint32_t voff = __umul24((uint32_t)min(dk_row[i], last), row_bytes) + dk_c[i] * 2;
+            const uint32_t dst =
+                (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds_addr(kd) + 1024 * (wave + NW * i)));
+            lds_dma16_sv(uniform_ptr(kbase + toff), voff, dst);
+            lds_dma16_sv(uniform_ptr(vbase + toff), voff, dst + TILE * 2);
         }
     };
 
@@ -632,7 +637,6 @@ bwd_dq_kernel(BwdParams p) {
     f32x16 dqacc[DBLK];
 #pragma unroll
     for (int i = 0; i < DBLK; ++i) dqacc[i] = f32x16{};
-    auto wave_needs = [&](int t) { return wave_live && t * BN < wave_kend; };
 
     if (ntiles > 0) {
         dma_tile(0, 0);
@@ -641,7 +645,6 @@ bwd_dq_kernel(BwdParams p) {
     for (int t = 0; t < ntiles; ++t) {
         wait_barrier<NLOAD>();  // tile t has landed; every wave is done with tile t-1
         dma_tile(t + 2, (t + 2) % NSLOT);
-        if (!wave_needs(t)) continue;
         const __bf16 *kt = ring + (t % NSLOT) * 2 * TILE;
         const __bf16 *vt = kt + TILE;
         // S^T = K Q^T, dP^T = V dO^T: keys kb*32 + 8 (j/4) + 4 half + j%4, row col.
@@ -662,22 +665,26 @@ bwd_dq_kernel(BwdParams p) {
             }
         }
         // dS^T = P^T (dP^T - D), P^T = 2^(s c - L); masked keys give P = 0.
-        const bool full = (t + 1) * BN <= wave_kfull;
+        float pv[KB][16];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) pv[kb][j] = fast_exp2(fmaf(sacc[kb][j], c, -lrow));
+        if ((t + 1) * BN > wave_kfull) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int key = t * BN + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+                    pv[kb][j] = key < row_kend ? pv[kb][j] : 0.f;
+                }
+        }
         bf16x8 dsf[KB][2];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int j = 8 * h2 + e;
-                    float pv = fast_exp2(fmaf(sacc[kb][j], c, -lrow));
-                    if (!full) {
-                        const int key = t * BN + kb * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-                        pv = key < row_kend ? pv : 0.f;
-                    }
-                    dsf[kb][h2][e] = (__bf16)(pv * (dpacc[kb][j] - drow));
-                }
+            for (int j = 0; j < 16; ++j)
+                dsf[kb][j >> 3][j & 7] = (__bf16)(pv[kb][j] * (dpacc[kb][j] - drow));
         // dQ^T += K^T dS^T (A = K^T by transposing reads).
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)

@@ -84,6 +84,14 @@ __device__ __forceinline__ void lds_dma16_sv(const void *sbase, uint32_t voff, u
                  : "s"(lds_base), "v"(voff), "s"(sbase)
                  : "memory", "m0");
 }
+// A wave-uniform pointer the compiler may hold in vector registers (a loop
+// induction variable, say), read from the first lane into scalar registers.
+__device__ __forceinline__ const void *uniform_ptr(const void *p) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    return (const void *)(uintptr_t)(lo | hi << 32);
+}
 #pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
