@@ -178,8 +178,7 @@ bwd_dkdv_kernel(BwdParams p) {
     const int tid = threadIdx.x;
     // wave-uniform wave index (scalar register): per-wave conditions are
     // scalar branches
-    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int col = lane & 31, half = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wave_u = wave;
 
     // ---- workgroup -> (sequence, K/V head, key block, row chunk) ----
@@ -189,7 +188,7 @@ bwd_dkdv_kernel(BwdParams p) {
     // causal mask) first, and a key block's row chunks together.
     const int pid = blockIdx.x;
     const int n_grp = p.B * p.Hkv;
-    const int n_inner = p.n_kb * p.n_ch;
+    const int n_inner = p.pair ? (p.n_kb + 1) / 2 : p.n_kb * p.n_ch;
     int grp, inner;
     if ((n_grp & 7) == 0) {
         const int slot = pid >> 3;
@@ -199,14 +198,35 @@ bwd_dkdv_kernel(BwdParams p) {
         grp = pid / n_inner;
         inner = pid % n_inner;
     }
-    const int kblk = inner / p.n_ch, chunk = inner - kblk * p.n_ch;
     const int b = grp / p.Hkv, kvh = grp - b * p.Hkv;
+    // Paired mode (causal, unchunked): key block i and its mirror
+    // n_kb(b) - 1 - i, one after the other, so that every workgroup walks
+    // about the same number of rows (the first block sees the most rows,
+    // its mirror the fewest).
+    int npass = 1, kb_first = inner / p.n_ch, chunk = inner - kb_first * p.n_ch, kb_second = -1;
+    if (p.pair) {
+        const int Lk_b = VARLEN ? p.cu_k[b + 1] - p.cu_k[b] : p.Sk;
+        const int nkb = (Lk_b + 127) / 128;
+        if (inner >= (nkb + 1) / 2) return;  // uniform over the workgroup
+        kb_first = inner;
+        chunk = 0;
+        kb_second = nkb - 1 - inner;
+        npass = kb_second > kb_first ? 2 : 1;
+    }
+    for (int pass = 0; pass < npass; ++pass) {
+    if (pass > 0) __syncthreads();  // every wave is done with the ring and V rows
+    int kblk = pass == 0 ? kb_first : kb_second;
+    int lane_r = tid & 63;
+    // opaque per pass: nothing derived from the lane or the block is kept
+    // live across passes (that would raise the register count of the loop)
+    asm volatile("" : "+s"(kblk), "+v"(lane_r));
+    const int lane = lane_r, col = lane & 31, half = lane >> 5;
     const KeyBlockRows kr = key_block_rows<CAUSAL, VARLEN>(p, b, kblk);
     const int q_tok0 = kr.q_tok0, Lq = kr.Lq, k_tok0 = kr.k_tok0, Lk = kr.Lk;
     const int k0 = kblk * 128;
-    if (k0 >= Lk) return;  // uniform over the workgroup
+    if (k0 >= Lk) continue;  // uniform over the workgroup
     const int n_valid = key_block_chunks(p, kr);
-    if (chunk >= n_valid) return;  // uniform: an empty row chunk
+    if (chunk >= n_valid) continue;  // uniform: an empty row chunk
     const int G = p.G;
     const int shift = Lk - Lq;
     const int rows_total = Lq * G;
@@ -418,7 +438,7 @@ bwd_dkdv_kernel(BwdParams p) {
 
     // ---- write dK = scale dK^T^T and dV: lane owns key kk, head_dim
     // elements 32 i + 8 g + 4 half .. +3 (or this chunk's fp32 partials) ----
-    if (!key_ok) return;
+    if (!key_ok) continue;
     if (n_valid > 1) {
         float *pk = p.ws_part + ((int64_t)(grp * p.n_kb + kblk) * p.n_ch + chunk) * (2 * 128 * D) +
                     (32 * wave + col) * D + 4 * half;
@@ -436,7 +456,7 @@ bwd_dkdv_kernel(BwdParams p) {
                 *(f32x4 *)(pk + i * 32 + 8 * g) = wk;
                 *(f32x4 *)(pv + i * 32 + 8 * g) = wv;
             }
-        return;
+        continue;
     }
     const int64_t off = ((int64_t)(k_tok0 + kk) * p.Hkv + kvh) * D + 4 * half;
     __bf16 *dkrow = (__bf16 *)p.dk + off;
@@ -454,6 +474,7 @@ bwd_dkdv_kernel(BwdParams p) {
             *(u32x2 *)(dkrow + i * 32 + 8 * g) = __builtin_bit_cast(u32x2, wk);
             *(u32x2 *)(dvrow + i * 32 + 8 * g) = __builtin_bit_cast(u32x2, wv);
         }
+    }  // pass
 }
 
 // ---------------------------------------------------------------------------
@@ -726,8 +747,15 @@ hipError_t launch_t(const BwdParams &p, hipStream_t s) {
     }
     const long long kv_blocks = (long long)p.B * p.Hkv * p.n_kb;
     if (kv_blocks > 0) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN>),
-                           dim3((unsigned)(kv_blocks * p.n_ch)), dim3(NTHREADS), 0, s, p);
+        // Under a causal mask key block i sees far more rows than the last
+        // ones: pair block i with n_kb - 1 - i in one workgroup so that the
+        // workgroups are about equally long (unless the rows are chunked).
+        BwdParams pk = p;
+        pk.pair = CAUSAL && p.n_ch == 1;
+        const long long grid = pk.pair ? (long long)p.B * p.Hkv * ((p.n_kb + 1) / 2)
+                                       : kv_blocks * p.n_ch;
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)grid),
+                           dim3(NTHREADS), 0, s, pk);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (p.n_ch > 1) {

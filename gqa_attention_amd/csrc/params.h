@@ -76,6 +76,9 @@ struct BwdParams {
     // into dK/dV by a reduction pass.
     int n_ch, ch_tiles;
     float *ws_part;
+    // Paired key blocks (causal, n_ch = 1): a dK/dV workgroup takes key block
+    // i and then n_kb(b) - 1 - i; the grid has (n_kb + 1) / 2 per head group.
+    int pair;
 };
 
 // Launchers (one per kernel family). Each returns a hipError_t.
