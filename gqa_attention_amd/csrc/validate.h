@@ -190,7 +190,10 @@ inline int decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen_k, in
         return 0;
     const long long units = (long long)B * Hkv * ((Hq / Hkv + 15) / 16);
     int ns = units >= 192 ? 1 : units >= 96 ? 2 : units >= 48 ? 4 : units >= 12 ? 8 : 16;
-    if (ragged && ns < 2) ns = 2;
+    // a window of at most half the longest length caps most visible ranges
+    // at the same length, so the batch is no longer ragged in what it reads
+    const bool window_evens = window_left >= 0 && 2LL * (window_left + 1) <= max_seqlen_k;
+    if (ragged && !window_evens && ns < 2) ns = 2;
     const long long keys = window_left >= 0 && (long long)window_left + 1 < max_seqlen_k
                                ? (long long)window_left + 1
                                : max_seqlen_k;

@@ -204,7 +204,9 @@ int gqa_attn_decode_ex(const void *q, const void *k_cache, const void *v_cache, 
  * split; splits are added until there are about 192 or more of them
  * (units >= 192 -> 1, >= 96 -> 2, >= 48 -> 4, >= 12 -> 8, else 16). A ragged
  * batch (ragged != 0: per-sequence lengths that differ) takes at least 2, so
- * that its longest sequences are cut and scheduled first. The count is then
+ * that its longest sequences are cut and scheduled first, unless a sliding
+ * window of at most half of max_seqlen_k evens the visible ranges out (most
+ * sequences then see exactly window_left + 1 keys). The count is then
  * halved while a split would get fewer than 512 keys of the longest visible
  * range (max_seqlen_k, or window_left + 1 when smaller). On the split-count
  * sweep of bf16 caches (B 1..128, 512..32768 keys, d 64 and 128) this choice

@@ -223,6 +223,9 @@ def test_decode_num_splits_rule():
     assert f(4, 48, 1, 64, 32768) == 8
     assert f(64, 32, 8, 128, 8192, ragged=True) == 2   # ragged: at least 2 splits
     assert f(64, 32, 8, 128, 800, ragged=True) == 1    # ... unless splits get < 512 keys
+    # ... or a window of at most half the longest length evens the ranges out
+    assert f(32, 32, 8, 128, 16384, 4095, ragged=True) == 1
+    assert f(32, 32, 8, 128, 6000, 4095, ragged=True) == 2
     for bad in [(0, 32, 8, 128, 10), (1, 30, 8, 128, 10), (1, 32, 8, 96, 10),
                 (1, 32, 8, 128, 0), (1, 32, 8, 128, 10, -2)]:
         assert f(*bad) == 0, bad
