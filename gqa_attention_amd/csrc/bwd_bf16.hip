@@ -26,11 +26,16 @@
 //    The page instead adds dQ atomically from the key-block pass; fp32
 //    atomics at this scale (one update per key block per dQ element) would
 //    cost more than the second pass's recomputation on this chip.
-//  * Q/dO and K/V tiles stream through a 3-slot LDS ring with direct
-//    global->LDS loads issued two tiles ahead, one barrier per tile. Rows are
-//    unpadded with an XOR swizzle of the 16-byte chunk index chosen so that
-//    both the row-slice reads and the transposing reads of a tile are free of
-//    bank conflicts.
+//  * Q/dO and K/V tiles stream through an LDS ring (3 slots; 2 for Q/dO at
+//    d = 128) with direct global->LDS loads issued ahead, one barrier per
+//    tile. Rows are unpadded with an XOR swizzle of the 16-byte chunk index
+//    chosen so that both the row-slice reads and the transposing reads of a
+//    tile are free of bank conflicts.
+//  * One code path per tile in both kernels: every wave runs every tile of
+//    its workgroup, with the element mask (a wave-uniform branch) only where
+//    the causal diagonal or a ragged end crosses the tile. Under a causal
+//    mask a dK/dV workgroup takes key block i and then n_kb - 1 - i, so the
+//    workgroups walk about the same number of rows.
 
 #include "device_util.h"
 #include "params.h"

@@ -21,17 +21,21 @@
 //  * 4 (d = 64) or 8 (d = 128) wavefronts x 32 packed rows;
 //    v_mfma_f32_32x32x16_bf16 computes the
 //    transposed score tile S^T = K Q^T so that each lane owns one query row:
-//    the row max and row sum are in-lane plus one v_permlane32_swap.
+//    a row max or row sum is in-lane plus one v_permlane32_swap.
 //  * O^T = V^T P^T accumulates with the same lane <-> query ownership, so the
 //    rescale by exp(m_old - m_new) is a per-lane scalar multiply and P never
 //    leaves registers (its bf16 copy is the B operand as produced).
+//  * The reference max m is the exact max of tile 0 and moves only when a
+//    tile's probabilities grow past a bound (then that tile is recomputed
+//    against the raised m); any reference gives the same result, since m
+//    cancels between O~ and l and is added back in L.
 //  * K and V are staged row-major in LDS by direct global->LDS loads of whole
-//    rows (no staging registers); the V^T operand is read with
-//    ds_read_b64_tr_b16, which hands each lane a column slice.
-//    Double-buffered and software-pipelined: the scores
-//    of tile t+1 run on the matrix cores while the vector units exponentiate
-//    tile t, with the global loads of the following tiles in flight (one
-//    barrier per tile).
+//    rows (no staging registers) into a 4-slot ring per tensor, 3 tiles
+//    ahead; the V^T operand is read with ds_read_b64_tr_b16, which hands each
+//    lane a column slice. Software-pipelined: the scores of tile t+1 run on
+//    the matrix cores while the vector units exponentiate tile t (one barrier
+//    per tile, one code path: every wave runs every tile of its workgroup,
+//    masked where it lies past the wave's causal limit).
 //  * exp is 2^x on the transcendental unit with scale*log2(e) folded into one
 //    FMA; P and O are rounded to bf16 with round-to-nearest-even.
 //  * Workgroup order: the row tiles of a head group run back to back on one
