@@ -56,10 +56,17 @@ def fwd_flops(lq: int, lk: int, hq: int, d: int, causal: bool) -> int:
 
 
 def source_digest(files) -> str:
+    """Digest of the kernel sources' code: comments and blank lines are left
+    out, so a comment edit does not void counters taken on the same code."""
+    import re
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 

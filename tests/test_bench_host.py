@@ -26,3 +26,14 @@ def test_multi_gpu_request_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_source_digest_ignores_comments_not_code(tmp_path):
+    a = tmp_path / "a.hip"
+    b = tmp_path / "b.hip"
+    c = tmp_path / "c.hip"
+    a.write_text("int f(int x) {\n    return x + 1;\n}\n")
+    b.write_text("// header\nint f(int x) {  /* note */\n\n    return x + 1;  // inc\n}\n")
+    c.write_text("int f(int x) {\n    return x + 2;\n}\n")
+    assert bench.source_digest([str(a)]) == bench.source_digest([str(b)])
+    assert bench.source_digest([str(a)]) != bench.source_digest([str(c)])
