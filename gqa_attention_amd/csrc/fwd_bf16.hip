@@ -460,10 +460,15 @@ fwd_bf16_kernel(FwdParams p) {
 
     // ---- epilogue: one division by l, L = m + log(l) ----
     const float l_tot = pair_sum32(l_run);
-    if (!row_ok) return;
     const bool empty = !(l_tot > 0.f);
     const float inv = empty ? 0.f : 1.f / l_tot;
-    __bf16 *orow = (__bf16 *)p.o + ((int64_t)(q_tok0 + pos) * p.Hq + head) * D + 4 * half;
+    // O leaves through this wave's own 32 rows of Qs (its Q fragment was read
+    // from there before the loop; no other wave touches them): lane (col, half)
+    // writes its 8-byte pieces of row col, then every lane reads whole 16-byte
+    // chunks, so each global store instruction writes 64 x 16 bytes in runs of
+    // full D-element rows rather than 32 rows x 16 bytes. Chunk c of row r
+    // sits in slot c ^ (r mod C8) to spread the row-strided writes over banks.
+    __bf16 *ow = Qs + wave * 32 * D;
 #pragma unroll
     for (int i = 0; i < DBLK; ++i)
 #pragma unroll
@@ -471,8 +476,23 @@ fwd_bf16_kernel(FwdParams p) {
             bf16x4 w;
 #pragma unroll
             for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[i][4 * g + e] * inv);
-            *(u32x2 *)(orow + i * 32 + 8 * g) = __builtin_bit_cast(u32x2, w);
+            const int c = (4 * i + g) ^ (col & (C8 - 1));
+            *(u32x2 *)(ow + col * D + c * 8 + 4 * half) = __builtin_bit_cast(u32x2, w);
         }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's writes precede its reads
+#pragma unroll
+    for (int j = 0; j < 32 * C8 / 64; ++j) {
+        const int idx = lane + 64 * j;
+        const int r = idx / C8, c = idx % C8;
+        const u32x4 v = *(const u32x4 *)(ow + r * D + ((c ^ (r & (C8 - 1))) * 8));
+        const int rr = row0 + wave * 32 + r;
+        if (rr < rows_total) {
+            const int rp = rr / p.gpack;
+            const int rh = qh0 + (rr - rp * p.gpack);
+            *(u32x4 *)((__bf16 *)p.o + ((int64_t)(q_tok0 + rp) * p.Hq + rh) * D + c * 8) = v;
+        }
+    }
+    if (!row_ok) return;
     if (half == 0) {
         const float lse = empty ? -INFINITY : (m_run + __log2f(l_tot)) * kLn2;
         const int64_t li = VARLEN ? (int64_t)(q_tok0 + pos) * p.Hq + head
