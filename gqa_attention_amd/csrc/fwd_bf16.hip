@@ -245,6 +245,26 @@ fwd_bf16_kernel(FwdParams p) {
             asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
     auto barrier_lds = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+    // d = 64: near the end of the loop no DMA is issued for tiles past the
+    // last needed one (the prologue still loads tiles 0-3 and 0-2, clamped):
+    // the barrier then keeps in flight only the loads actually issued after
+    // K(t+2) and V(t+1), and the workgroup ends with nothing left to drain
+    // (1-2 % faster at d = 64; at d = 128 the extra branches cost more than
+    // they save).
+    constexpr bool TAIL_SKIP = D == 64;
+    static_assert(NDMA == 1, "the tail wait counts assume one DMA load per tensor and step");
+    auto barrier_tail = [](int keep) {
+        if (keep >= 4)
+            asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else if (keep == 3)
+            asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else if (keep == 2)
+            asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else if (keep == 1)
+            asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
 
     // K operand (A of S^T = K Q^T): row kb*32 + col, chunk 2 s + half.
     int k_rd[DSTEPS];
@@ -406,8 +426,13 @@ fwd_bf16_kernel(FwdParams p) {
         constexpr int J = decltype(jc)::value;
         __bf16 *k_next = kslot(std::integral_constant<int, J + 1>{});  // K(t+1)
         __bf16 *v_cur = vslot(std::integral_constant<int, J>{});       // V(t)
-        dma_k(t + 4, kslot(std::integral_constant<int, J>{}));
-        dma_v(t + 3, vslot(std::integral_constant<int, J + 3>{}));
+        const bool tail = TAIL_SKIP && t + 4 >= ntiles;  // within the last four steps
+        if (!tail) {
+            dma_k(t + 4, kslot(std::integral_constant<int, J>{}));
+            dma_v(t + 3, vslot(std::integral_constant<int, J + 3>{}));
+        } else if (t + 3 < ntiles) {
+            dma_v(t + 3, vslot(std::integral_constant<int, J + 3>{}));
+        }
         bf16x8 pf[KB][2];
         bf16x8 vf[KB][2][DBLK];
         float l_tile;
@@ -443,7 +468,15 @@ fwd_bf16_kernel(FwdParams p) {
         l_run += l_tile;
         accumulate(vf, pf);
         mask(t + 1, s_nxt);
-        barrier_keep2();
+        if (!tail) {
+            barrier_keep2();
+        } else {
+            // loads issued after K(t+2) and V(t+1): K(t+3) and V(t+2) (by the
+            // prologue when t = 0), K(t+4) and V(t+3) (only if needed)
+            const int keep = (t + 3 < ntiles || t == 0) + (t + 2 < ntiles || t == 0) +
+                             (t + 4 < ntiles) + (t + 3 < ntiles);
+            barrier_tail(keep);
+        }
     };
     int t = 0;
     for (; t + 3 < ntiles; t += 4) {
