@@ -124,6 +124,35 @@ def test_bwd_varlen(case, d):
     print(case, d, errs)
 
 
+PAIRED = [
+    # B, Hq, Hkv, S, d: causal, B * Hkv * ceil(S / 128) >= 256 key blocks, so
+    # the rows are not chunked and a dK/dV workgroup takes key block i and
+    # then n_kb - 1 - i
+    (8, 8, 8, 512, 64),     # 4 key blocks per sequence: pairs (0, 3), (1, 2)
+    (8, 8, 8, 640, 64),     # 5: the middle block runs alone
+    (4, 16, 8, 1024, 128),  # GQA, 8 key blocks
+]
+
+
+@pytest.mark.parametrize("shape", PAIRED, ids=lambda s: "B{}_Hq{}_Hkv{}_S{}_d{}".format(*s))
+def test_bwd_paired_key_blocks(shape):
+    B, hq, hkv, S, d = shape
+    w = gqa_inputs.fixed(B, hq, hkv, S, S, d, seed=7000 + S + d, causal=True)
+    do = _dout(w, 83)
+    errs = compare_grads(run_bwd(w, do), oracle_bwd(w, do), f"bwd paired {shape}")
+    print(shape, errs)
+
+
+def test_bwd_paired_key_blocks_varlen():
+    """Paired key blocks over sequences of different lengths: each sequence
+    pairs its own key blocks (n_kb of the longest sizes the grid)."""
+    lens = [700, 130, 1, 640, 257, 0, 512, 385, 128, 600, 90, 700, 33, 256, 511, 640]
+    w = gqa_inputs.varlen(lens, lens, 8, 8, 64, seed=7100, causal=True)
+    do = _dout(w, 84)
+    errs = compare_grads(run_bwd(w, do), oracle_bwd(w, do), "bwd paired varlen")
+    print(errs)
+
+
 def test_bwd_rows_without_keys_get_zero_dq():
     """Causal with Lq > Lk: the first Lq - Lk rows see no key; their dq is
     exactly zero and the other rows' is not."""
