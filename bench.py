@@ -426,7 +426,7 @@ def main():
                            "gflop_per_step": round(r["flops"] / 1e9, 3)},
                 "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                             "traffic": None, "kernel": "bwd (pre + dkdv + dq)",
+                             "traffic": None, "kernel": "bwd (dq + dkdv)",
                              "launch_ms": round(r["avg_ms"], 5)}}
         print(json.dumps(line))
         return
@@ -521,7 +521,7 @@ def main():
             wb = loaders[name]()
             rb = bench_bwd(torch, ga, wb, 10, 2, **ramp)
             tf = rb["flops"] / (rb["avg_ms"] * 1e-3) / 1e12
-            extra.append({"workload": wb.name, "kernel": "bwd (pre + dkdv + dq)",
+            extra.append({"workload": wb.name, "kernel": "bwd (dq + dkdv)",
                           "pass": "backward", "tflops": round(tf, 2),
                           "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                           "ms_per_call": round(rb["avg_ms"], 5),

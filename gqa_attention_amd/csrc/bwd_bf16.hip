@@ -11,21 +11,21 @@
 // (D = rowsum(P * dP) because O = P V; the page prints no formulas.)
 //
 // gfx950 mapping (our design, not the pages'):
-//  * bwd_pre: one pass over O and dO gives D and L in log2 units for every
-//    (token, head), written in packed-row order (row rho = pos * G + head in
-//    group) so that a tile of 32 packed rows is 128 contiguous bytes.
+//  * bwd_dq runs first: a workgroup owns 128 packed rows (like the forward)
+//    and walks the key tiles: S^T = K Q^T and dP^T = V dO^T (each lane owns
+//    a query row, so L and D are per-lane scalars), dQ^T += K^T dS^T. Before
+//    its loop it forms D = rowsum(dO * O) and L in log2 units for its rows
+//    and stores them in packed-row order (row rho = pos * G + head in group),
+//    so that a tile of 32 packed rows is 128 contiguous bytes for the next
+//    pass. The page instead adds dQ atomically from the key-block pass; fp32
+//    atomics at this scale (one update per key block per dQ element) would
+//    cost more than the second pass's recomputation on this chip.
 //  * bwd_dkdv: a workgroup owns 128 keys of one K/V head (32 per wave, held
 //    as matrix-core operands in registers) and walks all packed rows of the
 //    G query heads of the group, so the GQA sum of dK and dV happens inside
 //    the accumulators. Per 32-row tile: S = Q K^T and dP = dO V^T (each lane
 //    owns a key), then dV^T += dO^T P and dK^T += Q^T dS, with the
 //    transposed operands dO^T and Q^T read by ds_read_b64_tr_b16.
-//  * bwd_dq: a workgroup owns 128 packed rows (like the forward) and walks
-//    the key tiles: S^T = K Q^T and dP^T = V dO^T (each lane owns a query
-//    row, so L and D are per-lane scalars), dQ^T += K^T dS^T.
-//    The page instead adds dQ atomically from the key-block pass; fp32
-//    atomics at this scale (one update per key block per dQ element) would
-//    cost more than the second pass's recomputation on this chip.
 //  * Q/dO and K/V tiles stream through an LDS ring (3 slots; 2 for Q/dO at
 //    d = 128) with direct global->LDS loads issued ahead, one barrier per
 //    tile. Rows are unpadded with an XOR swizzle of the 16-byte chunk index
@@ -81,45 +81,6 @@ __device__ __forceinline__ void wait_barrier() {
 // a multiple of 4 so that every group starts 16-byte aligned).
 __device__ __forceinline__ int64_t ws_base(const BwdParams &p, int b, int hgl) {
     return ((int64_t)b * (p.Hq / p.G) + hgl) * (((int64_t)p.Sq * p.G + 3) & ~(int64_t)3);
-}
-
-// ---------------------------------------------------------------------------
-// D = rowsum(dO * O) and L in log2 units, one row per D/8 lanes.
-// ---------------------------------------------------------------------------
-template <int D, bool VARLEN>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
-    constexpr int LPR = D / 8;        // lanes per row, 8 elements each
-    constexpr int RPB = 256 / LPR;    // rows per workgroup
-    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;  // (b, pos, head)
-    const int c = threadIdx.x % LPR;
-    if (row >= (int64_t)p.B * p.Sq * p.Hq) return;  // uniform over the row's lanes
-    const int head = (int)(row % p.Hq);
-    const int pos = (int)((row / p.Hq) % p.Sq);
-    const int b = (int)(row / ((int64_t)p.Hq * p.Sq));
-    int tok0 = b * p.Sq, Lq = p.Sq;
-    if (VARLEN) {
-        tok0 = p.cu_q[b];
-        Lq = p.cu_q[b + 1] - tok0;
-    }
-    if (pos >= Lq) return;
-    const int64_t off = ((int64_t)(tok0 + pos) * p.Hq + head) * D + 8 * c;
-    const u32x4 ow = *(const u32x4 *)((const __bf16 *)p.o + off);
-    const u32x4 gw = *(const u32x4 *)((const __bf16 *)p.dout + off);
-    const bf16x8 o8 = __builtin_bit_cast(bf16x8, ow), g8 = __builtin_bit_cast(bf16x8, gw);
-    float acc = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)o8[e], (float)g8[e], acc);
-#pragma unroll
-    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-    if (c == 0) {
-        const int64_t li = VARLEN ? (int64_t)(tok0 + pos) * p.Hq + head
-                                  : ((int64_t)b * p.Hq + head) * p.Sq + pos;
-        const float l = p.lse[li];
-        const int hgl = head / p.G;
-        const int64_t wi = ws_base(p, b, hgl) + (int64_t)pos * p.G + (head - hgl * p.G);
-        p.ws_d[wi] = acc;
-        p.ws_l[wi] = l == -INFINITY ? INFINITY : l * kLog2e;
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -587,24 +548,40 @@ bwd_dq_kernel(BwdParams p) {
     // past the end have L = +inf (P = 0) and are never stored.
     const int wave_kfull = CAUSAL ? min(Lk, (row0 + wave * 32) / G + 1 + shift) : Lk;
 
-    // Per-row statistics and the Q^T / dO^T fragments (B operands).
+    // Per-row statistics and the Q^T / dO^T fragments (B operands). This
+    // pass also forms the row statistics for the key-block pass that follows
+    // it: D = rowsum(dO * O) (the lane's half of the row, then its partner
+    // lane's) and L in log2 units (+inf for a row that sees no key, so that
+    // P = 0 there), stored in packed-row order.
     float lrow = INFINITY, drow = 0.f;
     bf16x8 qf[DSTEPS], gf[DSTEPS];
     {
-        if (row_ok) {
-            const int64_t wi = ws_base(p, b, kvh) + rho;
-            lrow = p.ws_l[wi];
-            drow = p.ws_d[wi];
-        }
         const int qpos = row_ok ? pos : Lq - 1;
         const int qhead = row_ok ? head : qh0;
         const int64_t off = ((int64_t)(q_tok0 + qpos) * p.Hq + qhead) * D + 8 * half;
+        float acc = 0.f;
 #pragma unroll
         for (int s = 0; s < DSTEPS; ++s) {
             const u32x4 a = *(const u32x4 *)((const __bf16 *)p.q + off + 16 * s);
             const u32x4 g2 = *(const u32x4 *)((const __bf16 *)p.dout + off + 16 * s);
+            const u32x4 o2 = *(const u32x4 *)((const __bf16 *)p.o + off + 16 * s);
             qf[s] = __builtin_bit_cast(bf16x8, row_ok ? a : u32x4{0u, 0u, 0u, 0u});
             gf[s] = __builtin_bit_cast(bf16x8, row_ok ? g2 : u32x4{0u, 0u, 0u, 0u});
+            const bf16x8 o8 = __builtin_bit_cast(bf16x8, o2);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = fmaf((float)o8[e], (float)gf[s][e], acc);
+        }
+        drow = pair_sum32(acc);
+        if (row_ok) {
+            const int64_t li = VARLEN ? (int64_t)(q_tok0 + pos) * p.Hq + head
+                                      : ((int64_t)b * p.Hq + head) * p.Sq + pos;
+            const float l = p.lse[li];
+            lrow = l == -INFINITY ? INFINITY : l * kLog2e;
+            if (half == 0) {
+                const int64_t wi = ws_base(p, b, kvh) + rho;
+                p.ws_d[wi] = drow;
+                p.ws_l[wi] = lrow;
+            }
         }
         u32x4 x = __builtin_bit_cast(u32x4, qf[0]) ^ __builtin_bit_cast(u32x4, gf[0]);
 #pragma unroll
@@ -744,11 +721,12 @@ bwd_dq_kernel(BwdParams p) {
 
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_t(const BwdParams &p, hipStream_t s) {
-    constexpr int RPB = 256 / (D / 8);
-    const long long pre_rows = (long long)p.B * p.Sq * p.Hq;
-    if (pre_rows > 0) {
-        hipLaunchKernelGGL((bwd_pre_kernel<D, VARLEN>), dim3((unsigned)((pre_rows + RPB - 1) / RPB)),
-                           dim3(256), 0, s, p);
+    // dQ first: it also writes the row statistics D and L that the key-block
+    // pass reads.
+    const long long q_grid = (long long)p.n_hg * p.n_rb;
+    if (q_grid > 0) {
+        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)q_grid),
+                           dim3(NTHREADS), 0, s, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -771,12 +749,6 @@ hipError_t launch_t(const BwdParams &p, hipStream_t s) {
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-    }
-    const long long q_grid = (long long)p.n_hg * p.n_rb;
-    if (q_grid > 0) {
-        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)q_grid),
-                           dim3(NTHREADS), 0, s, p);
-        return hipGetLastError();
     }
     return hipSuccess;
 }
