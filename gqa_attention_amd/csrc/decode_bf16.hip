@@ -149,10 +149,14 @@ decode_bf16_kernel(DecodeParams p) {
     // Q^T fragment (B operand): head_dim elements 32*s + 8*kq + j of query qi.
     bf16x8 qf[NS];
     {
-        const __bf16 *qrow = (const __bf16 *)p.q + ((int64_t)b * p.Hq + head) * D + 8 * kq;
+        // k-step s of lane group kq holds head_dim elements 8 kq + 32 s .. +7
+        // (bf16 cache) or 8 NS kq + 8 s .. +7 (fp8 cache, so that a lane's K
+        // codes for all steps are one contiguous run); K follows the same map.
+        const __bf16 *qrow = (const __bf16 *)p.q + ((int64_t)b * p.Hq + head) * D +
+                             (FP8 ? 8 * NS * kq : 8 * kq);
 #pragma unroll
         for (int s = 0; s < NS; ++s)
-            qf[s] = q_ok ? *(const bf16x8 *)(qrow + 32 * s)
+            qf[s] = q_ok ? *(const bf16x8 *)(qrow + (FP8 ? 8 * s : 32 * s))
                          : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
 
@@ -161,7 +165,8 @@ decode_bf16_kernel(DecodeParams p) {
     // Lane bases fold in the head and the lane's fixed column.
     const int64_t row_bytes = (int64_t)p.Hkv * D * ESZ;
     const int64_t head_off = (int64_t)kvh * D * ESZ + (PAGED ? 0 : (int64_t)b * p.Sk * row_bytes);
-    const unsigned char *kbase = (const unsigned char *)p.k + head_off + 8 * kq * ESZ;
+    const unsigned char *kbase =
+        (const unsigned char *)p.k + head_off + (FP8 ? 8 * NS * kq : 8 * kq) * ESZ;
     const unsigned char *vbase = (const unsigned char *)p.v + head_off + (lane % VCPR) * 16;
     const int lb = PAGED ? p.log2_block : 0;
     const int64_t page_bytes = row_bytes << lb;
@@ -188,8 +193,18 @@ decode_bf16_kernel(DecodeParams p) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             const unsigned char *krow = key_ptr(kbase, min(t0 + 16 * kt + qi, w_hi - 1));
+            if constexpr (FP8) {
+                // the lane's 8 NS codes are contiguous: 16-byte loads
 #pragma unroll
-            for (int s = 0; s < NS; ++s) kd[kt][s] = *(const kraw_t *)(krow + 32 * s * ESZ);
+                for (int h = 0; h < NS / 2; ++h) {
+                    const u32x4 w = *(const u32x4 *)(krow + 16 * h);
+                    kd[kt][2 * h] = kraw_t{w[0], w[1]};
+                    kd[kt][2 * h + 1] = kraw_t{w[2], w[3]};
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < NS; ++s) kd[kt][s] = *(const kraw_t *)(krow + 32 * s * ESZ);
+            }
         }
 #pragma unroll
         for (int i = 0; i < NVL; ++i) {
