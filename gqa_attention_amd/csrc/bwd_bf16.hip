@@ -120,8 +120,14 @@ __device__ __forceinline__ int key_block_chunks(const BwdParams &p, const KeyBlo
     return min(p.n_ch, max(1, (r.t_hi - r.t_lo + p.ch_tiles - 1) / p.ch_tiles));
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2))) void
+// ONE: the variant for grids of at most one workgroup per CU (a causal
+// prefill of one sequence with few K/V heads: B Hkv n_kb / 2 workgroups). Each
+// SIMD then runs a single wave, which must hide its own LDS latency: the
+// register budget is 512 (one wave per SIMD), V stays in registers at every
+// head dim, the ring has 3 slots, and every LDS operand of a tile is read
+// ahead of the products that use it.
+template <int D, bool CAUSAL, bool VARLEN, bool ONE>
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(ONE ? 1 : 2))) void
 bwd_dkdv_kernel(BwdParams p) {
     constexpr int BR = 32;             // packed rows per tile
     constexpr int C8 = D / 8;          // 16-byte chunks per row
@@ -136,7 +142,7 @@ bwd_dkdv_kernel(BwdParams p) {
     // d = 128: the V operand lives in LDS (its 32 VGPRs would spill next to
     // the two 64-VGPR accumulators), and a 2-slot ring keeps two workgroups
     // per CU; d = 64: V in registers, 3-slot ring.
-    constexpr bool VLDS = D == 128;
+    constexpr bool VLDS = D == 128 && !ONE;
     constexpr int NS = VLDS ? 2 : NSLOT;
     __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * SLOT];
     __shared__ __attribute__((aligned(16))) __bf16 vlds[VLDS ? NW * 32 * D : 8];
@@ -339,6 +345,45 @@ bwd_dkdv_kernel(BwdParams p) {
 
         // S = Q K^T and dP = dO V^T: rows 8 (j/4) + 4 half + j%4, key col.
         f32x16 sacc = f32x16{}, dpacc = f32x16{};
+        // ONE: the tile's transposed operands (A of dV^T and dK^T), read
+        // ahead of the exponentials
+        bf16x8 tg[ONE ? 2 : 1][ONE ? DBLK : 1], tq[ONE ? 2 : 1][ONE ? DBLK : 1];
+        if constexpr (ONE) {
+            bf16x8 qa[DSTEPS], ga[DSTEPS];
+#pragma unroll
+            for (int s = 0; s < DSTEPS; ++s) {
+                qa[s] = *(const bf16x8 *)(qt + (rs_b ^ (16 * s)));
+                ga[s] = *(const bf16x8 *)(gt + (rs_b ^ (16 * s)));
+            }
+#pragma unroll
+            for (int s = 0; s < DSTEPS; ++s)
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[s], sacc, 0, 0, 0);
+#pragma unroll
+            for (int s = 0; s < DSTEPS; ++s)
+                dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[s], vf[s], dpacc, 0, 0, 0);
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < DBLK; ++i) {
+                    const int tri = tr_b ^ (32 * i);
+                    const int o = 16 * h2 * D + tri, o8 = 16 * h2 * D + (tri ^ 16) + 8 * D;
+                    const u32x2 g0 = lds_read_tr16(gt + o), g1 = lds_read_tr16(gt + o8);
+                    const u32x2 q0 = lds_read_tr16(qt + o), q1 = lds_read_tr16(qt + o8);
+                    tg[h2][i] = __builtin_bit_cast(bf16x8, u32x4{g0[0], g0[1], g1[0], g1[1]});
+                    tq[h2][i] = __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]});
+                }
+            // Issue order: the row slices of both products, then each product
+            // MFMA followed by a share of the remaining reads (transposed
+            // operands, then L and D), so that one wave keeps the LDS busy
+            // while its matrix core runs.
+            constexpr int NTR = 2 * 2 * DBLK * 2 + 8;  // transposing reads + L/D reads
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * DSTEPS, 0);
+#pragma unroll
+            for (int g = 0; g < 2 * DSTEPS; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, (NTR + 2 * DSTEPS - 1) / (2 * DSTEPS), 0);
+            }
+        } else {
 #pragma unroll
         for (int s = 0; s < DSTEPS; ++s) {
             const bf16x8 a = *(const bf16x8 *)(qt + (rs_b ^ (16 * s)));
@@ -353,6 +398,7 @@ bwd_dkdv_kernel(BwdParams p) {
             else
                 bv = vf[s];
             dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bv, dpacc, 0, 0, 0);
+        }
         }
         // P = 2^(s c - L), dS = P (dP - D); masked pairs and rows past the end
         // give P = 0. B operands for k-step h2: rows 16 h2 + 8 (e/4) + 4 half + e%4.
@@ -386,6 +432,15 @@ bwd_dkdv_kernel(BwdParams p) {
             dsf[j >> 3][j & 7] = (__bf16)dsv[j];
         }
         // dV^T += dO^T P, dK^T += Q^T dS (A operands by transposing reads).
+        if constexpr (ONE) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < DBLK; ++i) {
+                    dvacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tg[h2][i], pf[h2], dvacc[i], 0, 0, 0);
+                    dkacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[h2][i], dsf[h2], dkacc[i], 0, 0, 0);
+                }
+        } else
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -719,6 +774,15 @@ bwd_dq_kernel(BwdParams p) {
         }
 }
 
+// Compute units of the current device (256 on MI355X).
+int device_cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 256;
+    return n;
+}
+
 template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_t(const BwdParams &p, hipStream_t s) {
     // dQ first: it also writes the row statistics D and L that the key-block
@@ -739,8 +803,14 @@ hipError_t launch_t(const BwdParams &p, hipStream_t s) {
         pk.pair = CAUSAL && p.n_ch == 1;
         const long long grid = pk.pair ? (long long)p.B * p.Hkv * ((p.n_kb + 1) / 2)
                                        : kv_blocks * p.n_ch;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)grid),
-                           dim3(NTHREADS), 0, s, pk);
+        // A grid of at most one workgroup per CU runs one wave per SIMD
+        // whatever the register budget: take the variant built for that.
+        if (D == 128 && grid <= device_cu_count())
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN, D == 128>), dim3((unsigned)grid),
+                               dim3(NTHREADS), 0, s, pk);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, VARLEN, false>), dim3((unsigned)grid),
+                               dim3(NTHREADS), 0, s, pk);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (p.n_ch > 1) {

@@ -131,6 +131,16 @@ PAIRED = [
     (8, 8, 8, 512, 64),     # 4 key blocks per sequence: pairs (0, 3), (1, 2)
     (8, 8, 8, 640, 64),     # 5: the middle block runs alone
     (4, 16, 8, 1024, 128),  # GQA, 8 key blocks
+    # more than 256 workgroups (one per CU on MI355X): the two-workgroups-per-CU
+    # variant of the key-block pass; the smaller grids above run the variant
+    # built for one workgroup per CU
+    (16, 8, 8, 640, 128),   # 16 * 8 * 3 pairs
+]
+
+BIG_GRID_FULL = [
+    # B, Hq, Hkv, S, d: non-causal, more than 256 key-block workgroups
+    (6, 8, 8, 700, 128),    # 6 * 8 * 6 key blocks, ragged last block
+    (6, 12, 4, 1100, 64),   # G = 3, 6 * 4 * 9
 ]
 
 
@@ -140,6 +150,15 @@ def test_bwd_paired_key_blocks(shape):
     w = gqa_inputs.fixed(B, hq, hkv, S, S, d, seed=7000 + S + d, causal=True)
     do = _dout(w, 83)
     errs = compare_grads(run_bwd(w, do), oracle_bwd(w, do), f"bwd paired {shape}")
+    print(shape, errs)
+
+
+@pytest.mark.parametrize("shape", BIG_GRID_FULL, ids=lambda s: "B{}_Hq{}_Hkv{}_S{}_d{}".format(*s))
+def test_bwd_big_grid_full(shape):
+    B, hq, hkv, S, d = shape
+    w = gqa_inputs.fixed(B, hq, hkv, S, S, d, seed=7200 + S + d, causal=False)
+    do = _dout(w, 85)
+    errs = compare_grads(run_bwd(w, do), oracle_bwd(w, do), f"bwd big grid {shape}")
     print(shape, errs)
 
 
