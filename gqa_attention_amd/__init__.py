@@ -10,6 +10,9 @@ Functions mirror the C entry points:
 
 * ``fwd(q, k, v, causal=False, scale=None, cu_seqlens_q=None, cu_seqlens_k=None,
   max_seqlen_q=None, max_seqlen_k=None)`` -> ``(out, lse)``
+* ``fwd_fp8(q, k, v, q_scale=1.0, k_scale=1.0, v_scale=1.0, causal=False, ...)`` ->
+  ``(out, lse)``: the forward over float8_e4m3fn inputs with per-tensor
+  dequantisation scales (bf16 out); ``FwdPlan(..., fp8_scales=(qs, ks, vs))``
 * ``decode(q, k_cache, v_cache, scale=None, num_splits=1, workspace=None)`` ->
   ``(out, lse)``
 * ``bwd(q, k, v, out, lse, dout, causal=False, scale=None, cu_seqlens_q=None,
@@ -73,6 +76,9 @@ def lib() -> ctypes.CDLL:
     L.gqa_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
                                vp, vp, i32, vp]
     L.gqa_attn_fwd.restype = i32
+    L.gqa_attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
+                                   vp, vp, f32, f32, f32, vp]
+    L.gqa_attn_fwd_fp8.restype = i32
     L.gqa_attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz,
                                   i32, vp]
     L.gqa_attn_decode.restype = i32
@@ -134,16 +140,22 @@ def _stream_handle(device) -> int:
 
 
 def _prepare_fwd(q, k, v, causal, scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                 max_seqlen_k, out, lse):
-    """Check tensor metadata, allocate outputs, build the C argument tuple."""
+                 max_seqlen_k, out, lse, fp8_scales=None):
+    """Check tensor metadata, allocate outputs, build the C argument tuple.
+
+    fp8_scales = (q_scale, k_scale, v_scale) for gqa_attn_fwd_fp8: q, k, v are
+    float8_e4m3fn and out is bfloat16."""
     dt = q.dtype
     varlen = cu_seqlens_q is not None or cu_seqlens_k is not None
     nd = 3 if varlen else 4
     dev = q.device
+    if fp8_scales is not None and dt != torch.float8_e4m3fn:
+        raise ValueError(f"q has dtype {dt}, expected torch.float8_e4m3fn")
     _check("q", q, nd, dt, None)
     _check("k", k, nd, dt, dev)
     _check("v", v, nd, dt, dev)
-    code = _dtype_code(q)
+    code = _dtype_code(q) if fp8_scales is None else None
+    out_dt = dt if fp8_scales is None else torch.bfloat16
     d = q.shape[-1]
     if k.shape[-1] != d or v.shape[-1] != d or k.shape != v.shape:
         raise ValueError("q, k, v head_dim and k/v shapes must agree")
@@ -169,9 +181,9 @@ def _prepare_fwd(q, k, v, causal, scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_
         lse_shape = (B, Hq, Sq)
         cq = ck = None
     if out is None:
-        out = torch.empty(q.shape, dtype=dt, device=dev)
+        out = torch.empty(q.shape, dtype=out_dt, device=dev)
     else:
-        _check("out", out, nd, dt, dev)
+        _check("out", out, nd, out_dt, dev)
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
     if lse is None:
@@ -182,7 +194,8 @@ def _prepare_fwd(q, k, v, causal, scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_
             raise ValueError(f"lse must have shape {lse_shape}")
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq,
-            Hkv, Sq, Sk, d, sc, int(bool(causal)), cq, ck, code)
+            Hkv, Sq, Sk, d, sc, int(bool(causal)), cq, ck)
+    args += (code,) if fp8_scales is None else tuple(float(x) for x in fp8_scales)
     return out, lse, args, q.numel() == 0
 
 
@@ -208,6 +221,28 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = Fal
     return out, lse
 
 
+def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, q_scale: float = 1.0,
+            k_scale: float = 1.0, v_scale: float = 1.0, causal: bool = False,
+            scale: Optional[float] = None, cu_seqlens_q: Optional[torch.Tensor] = None,
+            cu_seqlens_k: Optional[torch.Tensor] = None, max_seqlen_q: Optional[int] = None,
+            max_seqlen_k: Optional[int] = None, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention forward over fp8 e4m3 inputs through ``gqa_attn_fwd_fp8``.
+
+    q, k, v are torch.float8_e4m3fn tensors in the layouts of :func:`fwd`;
+    the values they stand for are code x q_scale (k_scale, v_scale). Returns
+    out (bfloat16, q's shape) and lse (fp32) as :func:`fwd` does.
+    """
+    out, lse, args, empty = _prepare_fwd(q, k, v, causal, scale, cu_seqlens_q, cu_seqlens_k,
+                                         max_seqlen_q, max_seqlen_k, out, lse,
+                                         (q_scale, k_scale, v_scale))
+    if not empty:
+        with torch.cuda.device(q.device):
+            st = lib().gqa_attn_fwd_fp8(*args, _stream_handle(q.device))
+        _raise(st, "gqa_attn_fwd_fp8")
+    return out, lse
+
+
 class FwdPlan:
     """A forward call with its arguments checked and marshalled once.
 
@@ -217,19 +252,21 @@ class FwdPlan:
     """
 
     def __init__(self, q, k, v, *, causal=False, scale=None, cu_seqlens_q=None,
-                 cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, out=None, lse=None):
+                 cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, out=None, lse=None,
+                 fp8_scales=None):
         self.out, self.lse, self._args, self._empty = _prepare_fwd(
             q, k, v, causal, scale, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-            out, lse)
+            out, lse, fp8_scales)
         self._keep = (q, k, v, cu_seqlens_q, cu_seqlens_k)
         self._dev = q.device
-        self._fn = lib().gqa_attn_fwd
+        self._name = "gqa_attn_fwd" if fp8_scales is None else "gqa_attn_fwd_fp8"
+        self._fn = getattr(lib(), self._name)
 
     def run(self):
         if not self._empty:
             st = self._fn(*self._args, _stream_handle(self._dev))
             if st:
-                _raise(st, "gqa_attn_fwd")
+                _raise(st, self._name)
         return self.out, self.lse
 
 

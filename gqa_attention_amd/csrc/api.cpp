@@ -2,6 +2,7 @@
 // grid, launch asynchronously on the caller's stream. Nothing here allocates,
 // synchronises or reads device memory.
 
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 
@@ -141,6 +142,48 @@ int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *
     if (dtype == GQA_DTYPE_BF16)
         return status_from(gqa::launch_fwd_bf16(p, d, causal != 0, varlen, s));
     return status_from(gqa::launch_fwd_f32(p, d, causal != 0, varlen, false, s));
+}
+
+int gqa_attn_fwd_fp8(const void *q, const void *k, const void *v, void *out, float *lse, int B,
+                     int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                     const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, float q_scale,
+                     float k_scale, float v_scale, void *stream) {
+    // same geometry rules as the bf16 forward (one byte per element instead
+    // of two only relaxes them)
+    const int rc = gqa::validate_fwd(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, d, scale,
+                                     cu_seqlens_q, cu_seqlens_k, GQA_DTYPE_BF16);
+    if (rc != GQA_OK) return rc;
+    if (!gqa::valid_dequant_scale(q_scale) || !gqa::valid_dequant_scale(k_scale) ||
+        !gqa::valid_dequant_scale(v_scale))
+        return GQA_EINVAL;
+    const float c = scale * q_scale * k_scale * 1.4426950408889634f;
+    if (!(c > 0.f) || !std::isfinite(c)) return GQA_EINVAL;
+    if (Sq == 0) return GQA_OK;
+    gqa::FwdParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = out;
+    p.lse = lse;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Sq = Sq;
+    p.Sk = Sk;
+    p.G = Hq / Hkv;
+    p.gpack = pack_enabled() ? p.G : 1;
+    p.n_hg = B * (Hq / p.gpack);
+    p.scale = scale;
+    p.scale_log2 = c;
+    p.o_scale = v_scale;
+    p.num_splits = 1;
+    const int rows = gqa::fwd_bf16_rows_per_tile(d);
+    p.n_rb = (int)(((long long)p.gpack * Sq + rows - 1) / rows);
+    (void)hipGetLastError();
+    return status_from(gqa::launch_fwd_fp8(p, d, causal != 0, cu_seqlens_q != nullptr,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache, void *out,

@@ -59,14 +59,6 @@ constexpr int MAX_TBL = 2048;
 constexpr int LPT_MAX = 256;
 static_assert(LPT_MAX <= NTHREADS, "one thread ranks one sequence");
 
-// fp8 e4m3 -> bf16 (exact) for 4 / 8 packed values.
-__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
-    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-    const bf2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
-    const bf2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
-    return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-}
-
 template <int D, bool PAGED, bool FP8>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(GQA_DEC_WPE))) void
 decode_bf16_kernel(DecodeParams p) {

@@ -12,6 +12,8 @@ typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+typedef uint32_t u32x8_t __attribute__((__vector_size__(8 * sizeof(uint32_t))));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -99,6 +101,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 
 // 2^x on the transcendental unit (v_exp_f32); exact 0 for -inf.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp8 e4m3 -> bf16 (exact: every e4m3 value is a bf16 value) for 4 packed
+// values.
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    const bf2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+    const bf2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+    return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
 
 // Pack the low / high bf16 halves of two dwords: (lo(a), lo(b)) and (hi(a), hi(b)).
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {

@@ -91,12 +91,26 @@ struct Cfg {
     static constexpr int C8 = D / 8;                    // 16-byte chunks per row
     static constexpr int NDMA = BN * D * 2 / 1024 / NW;  // DMA instructions per wave per tensor
     static __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+    // fp8 rows (D bytes, C16 = D / 16 chunks): 16 consecutive rows read at
+    // one chunk hit distinct bank groups (two rows per 256 bytes at d = 128,
+    // four at d = 64).
+    static __device__ __forceinline__ int swz8(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
     static __device__ __forceinline__ int swz_v(int r) {
         return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
     }
 };
 
-template <int D, bool CAUSAL, bool VARLEN>
+// F8: q, k, v hold fp8 e4m3 codes (one byte each) with per-tensor
+// dequantisation scales folded into scale_log2 (q_scale k_scale) and o_scale
+// (v_scale). The scores run on the fp8 matrix cores (32x32x64, exact products
+// summed in fp32). K and V tiles arrive together, one 16-byte direct load per
+// wave (half of the waves fetch K rows, half V rows), into one ring slot: K in
+// its lower half (fp8 rows, swizzled for the operand reads), V in its upper
+// half (unswizzled). One step before its use, the workgroup widens the V tile
+// exactly to bf16 into one of two bf16 V slots, so P stays bf16 and O^T += V^T
+// P^T runs as in the bf16 kernel: the result is the attention of the
+// dequantised inputs, rounded as in the bf16 path.
+template <int D, bool CAUSAL, bool VARLEN, bool F8>
 __global__ __launch_bounds__(Waves<D>::NTHREADS) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2))) void
 fwd_bf16_kernel(FwdParams p) {
     using CF = Cfg<D>;
@@ -115,8 +129,8 @@ fwd_bf16_kernel(FwdParams p) {
     __shared__ __attribute__((aligned(1024))) __bf16 Ks3[BN * D];
     __shared__ __attribute__((aligned(1024))) __bf16 Vs0[BN * D];
     __shared__ __attribute__((aligned(1024))) __bf16 Vs1[BN * D];
-    __shared__ __attribute__((aligned(1024))) __bf16 Vs2[BN * D];
-    __shared__ __attribute__((aligned(1024))) __bf16 Vs3[BN * D];
+    __shared__ __attribute__((aligned(1024))) __bf16 Vs2[F8 ? 8 : BN * D];  // F8: two bf16 V slots
+    __shared__ __attribute__((aligned(1024))) __bf16 Vs3[F8 ? 8 : BN * D];
     // The workgroup's Q rows, staged once by the same direct loads (K swizzle).
     __shared__ __attribute__((aligned(1024))) __bf16 Qs[BM * D];
     auto kslot = [&](auto j) -> __bf16 * {
@@ -124,7 +138,7 @@ fwd_bf16_kernel(FwdParams p) {
         return J == 0 ? Ks0 : J == 1 ? Ks1 : J == 2 ? Ks2 : Ks3;
     };
     auto vslot = [&](auto j) -> __bf16 * {
-        constexpr int J = decltype(j)::value & 3;
+        constexpr int J = decltype(j)::value & (F8 ? 1 : 3);
         return J == 0 ? Vs0 : J == 1 ? Vs1 : J == 2 ? Vs2 : Vs3;
     };
 
@@ -200,7 +214,9 @@ fwd_bf16_kernel(FwdParams p) {
     // start pays one memory latency rather than the Q load's and then the
     // first tiles'. Rows past the end are clamped to the last row (finite
     // values whose results are never stored).
-    bf16x8 qf[DSTEPS];
+    bf16x8 qf[F8 ? 1 : DSTEPS];
+    constexpr int DS8 = D / 64;  // F8: k-steps of the fp8 score product
+    i32x8 qf8[F8 ? DS8 : 1];
 
     const int64_t kv_stride = (int64_t)p.Hkv * D;
     const __bf16 *kbase = (const __bf16 *)p.k + ((int64_t)k_tok0 * p.Hkv + kvh) * D;
@@ -251,8 +267,40 @@ fwd_bf16_kernel(FwdParams p) {
     // K(t+2) and V(t+1), and the workgroup ends with nothing left to drain
     // (1-2 % faster at d = 64; at d = 128 the extra branches cost more than
     // they save).
-    constexpr bool TAIL_SKIP = D == 64;
+    constexpr bool TAIL_SKIP = D == 64 && !F8;
     static_assert(NDMA == 1, "the tail wait counts assume one DMA load per tensor and step");
+    // F8: K and V tile t into ring slot dst (K rows in its first BN D bytes,
+    // V rows in the next BN D bytes): wave w < NW/2 fetches 1024 bytes of K,
+    // wave NW/2 + w the same bytes of V; lane l covers 16-byte chunk
+    // (64 w' + l) % C16 of row (64 w' + l) / C16. K chunks are swizzled (slot
+    // c ^ swz8(r)), V chunks are not. Rows past kend are clamped as above.
+    constexpr int C16 = D / 16;  // 16-byte chunks per fp8 row
+    static_assert(!F8 || BN * D == 1024 * (NW / 2), "F8: one 16-byte load per wave and tile");
+    const uint32_t row_bytes8 = (uint32_t)kv_stride;  // fp8 row stride
+    const bool kv_is_v = wave >= NW / 2;               // wave-uniform
+    const int wk = kv_is_v ? wave - NW / 2 : wave;
+    const unsigned char *kv8base =
+        (const unsigned char *)(kv_is_v ? p.v : p.k) + ((int64_t)k_tok0 * p.Hkv + kvh) * D;
+    const int dma8_r = (64 * wk + lane) / C16;
+    const uint32_t dma8_c = (uint32_t)((((64 * wk + lane) % C16) ^ (kv_is_v ? 0 : CF::swz8(dma8_r))) * 16);
+    auto dma_kv8 = [&](int t, __bf16 *dst) {
+        const int tt = min(t, ntiles - 1);
+        const int last = kend - 1 - tt * BN;
+        const unsigned char *tile = kv8base + (uint64_t)(uint32_t)tt * (BN * row_bytes8);
+        const uint32_t lds0 = lds_addr(dst) + (kv_is_v ? BN * D : 0) + 1024 * wk;
+        lds_dma16_sv(tile, __umul24((uint32_t)min(dma8_r, last), row_bytes8) + dma8_c, lds0);
+    };
+    // F8: the two most recent KV groups (one load each) may stay in flight.
+    auto barrier_keep2_f8 = [] { asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+    // F8: widen V tile j (upper half of its ring slot, fp8) to bf16 in its V
+    // slot: thread x converts 8 values, row x / (D/8), elements 8 (x % (D/8)) ..
+    const int cv_row = tid / (D / 8), cv_part = tid % (D / 8);
+    static_assert(!F8 || Waves<D>::NTHREADS * 8 == BN * D, "F8: 8 V values per thread and tile");
+    auto widen_v = [&](const __bf16 *slot, __bf16 *vdst) {
+        const u32x2 raw = *(const u32x2 *)((const unsigned char *)slot + BN * D + tid * 8);
+        const u32x2 lo = fp8x4_to_bf16x4(raw[0]), hi = fp8x4_to_bf16x4(raw[1]);
+        *(u32x4 *)(vdst + cv_row * D + ((cv_part ^ CF::swz_v(cv_row)) * 8)) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
     auto barrier_tail = [](int keep) {
         if (keep >= 4)
             asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -270,6 +318,17 @@ fwd_bf16_kernel(FwdParams p) {
     int k_rd[DSTEPS];
 #pragma unroll
     for (int s = 0; s < DSTEPS; ++s) k_rd[s] = col * D + (((2 * s + half) ^ CF::swz_k(col)) * 8);
+    // F8 operand of k-step s: row col, bytes 64 s + 32 half .. +31 (logical
+    // chunks 4 s + 2 half and + 1), the same for K and Q so that the lanes'
+    // k indices of both operands agree; byte offsets.
+    int k8_rd[F8 ? 2 * DS8 : 1];
+    if constexpr (F8) {
+#pragma unroll
+        for (int s = 0; s < DS8; ++s)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                k8_rd[2 * s + e] = col * D + (((4 * s + 2 * half + e) ^ CF::swz8(col)) * 16);
+    }
     // V^T operand through ds_read_b64_tr_b16: in 16-lane group g, lane j reads
     // row key0 + j/4, columns d0 + 4 (j%4) .. +3 and receives column d0 + j of
     // rows key0 .. key0+3, with d0 = 32 i + 16 (g & 1) and key0 = 4 (g >> 1)
@@ -292,6 +351,24 @@ fwd_bf16_kernel(FwdParams p) {
 
     // S^T tile (rows = keys, columns = this wave's 32 query rows) from LDS.
     auto scores = [&](const __bf16 *ks, f32x16 (&sacc)[KB]) {
+        if constexpr (F8) {
+            const unsigned char *k8 = (const unsigned char *)ks;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                sacc[kb] = f32x16{};
+#pragma unroll
+                for (int s = 0; s < DS8; ++s) {
+                    const u32x4 lo = *(const u32x4 *)(k8 + kb * 32 * D + k8_rd[2 * s]);
+                    const u32x4 hi = *(const u32x4 *)(k8 + kb * 32 * D + k8_rd[2 * s + 1]);
+                    const i32x8 a = __builtin_bit_cast(
+                        i32x8, u32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+                    // formats 0 / 0: both operands fp8 e4m3; E8M0 scales 127 = 1
+                    sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8[s], sacc[kb], 0, 0,
+                                                                              0, 127, 0, 127);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             sacc[kb] = f32x16{};
@@ -392,7 +469,38 @@ fwd_bf16_kernel(FwdParams p) {
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
     f32x16 sa[KB], sb[KB];
-    if (ntiles > 0) {
+    if (ntiles > 0 && F8) {
+        // fp8 Q rows (D bytes each, swizzled as the K rows), then KV(0..3)
+        constexpr int NQ8 = BM * D / 1024 / NW;  // Q loads per wave
+#pragma unroll
+        for (int i = 0; i < NQ8; ++i) {
+            const int idx = 64 * (wave + NW * i) + lane;
+            const int r = idx / C16;
+            const int rho = min(row0 + r, rows_total - 1);
+            const int qp = rho / p.gpack;
+            const int qh = qh0 + (rho - qp * p.gpack);
+            const unsigned char *src = (const unsigned char *)p.q + ((int64_t)(q_tok0 + qp) * p.Hq + qh) * D +
+                                       ((idx % C16) ^ CF::swz8(r)) * 16;
+            lds_dma16(src, lds_addr(Qs) + 1024 * (wave + NW * i));
+        }
+        dma_kv8(0, kslot(I0{}));
+        dma_kv8(1, kslot(I1{}));
+        dma_kv8(2, kslot(I2{}));
+        dma_kv8(3, kslot(I3{}));
+        barrier_keep2_f8();  // Q, KV(0), KV(1) have landed
+        widen_v(kslot(I0{}), vslot(I0{}));
+        const unsigned char *q8 = (const unsigned char *)Qs + wave * 32 * D;
+#pragma unroll
+        for (int s = 0; s < DS8; ++s) {
+            const u32x4 lo = *(const u32x4 *)(q8 + k8_rd[2 * s]);
+            const u32x4 hi = *(const u32x4 *)(q8 + k8_rd[2 * s + 1]);
+            qf8[s] = __builtin_bit_cast(i32x8, u32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        }
+        scores(kslot(I0{}), sa);
+        mask(0, sa);
+        raise_max(sa);
+        barrier_lds();  // V(0) widened; K(0)'s slot is refilled with KV(4) in step 0
+    } else if (ntiles > 0) {
         constexpr int NQ = BM * D * 2 / 1024 / NW;  // Q loads per wave
 #pragma unroll
         for (int i = 0; i < NQ; ++i) {
@@ -427,7 +535,12 @@ fwd_bf16_kernel(FwdParams p) {
         __bf16 *k_next = kslot(std::integral_constant<int, J + 1>{});  // K(t+1)
         __bf16 *v_cur = vslot(std::integral_constant<int, J>{});       // V(t)
         const bool tail = TAIL_SKIP && t + 4 >= ntiles;  // within the last four steps
-        if (!tail) {
+        if constexpr (F8) {
+            // KV(t+4) into K(t)'s slot; V(t+1) (landed by the last barrier)
+            // widened into the bf16 V slot that V(t-1) used
+            dma_kv8(t + 4, kslot(std::integral_constant<int, J>{}));
+            widen_v(kslot(std::integral_constant<int, J + 1>{}), vslot(std::integral_constant<int, J + 1>{}));
+        } else if (!tail) {
             dma_k(t + 4, kslot(std::integral_constant<int, J>{}));
             dma_v(t + 3, vslot(std::integral_constant<int, J + 3>{}));
         } else if (t + 3 < ntiles) {
@@ -443,7 +556,7 @@ fwd_bf16_kernel(FwdParams p) {
             scores(k_next, s_nxt);
             load_v(v_cur, vf);
             probs(s_cur, pf, l_tile);
-            constexpr int NSM = KB * DSTEPS;    // score MFMAs
+            constexpr int NSM = KB * (F8 ? DS8 : DSTEPS);  // score MFMAs
             constexpr int NVR = 2 * KB * 2 * DBLK;  // transposing V reads
             constexpr int VALU_PER = (KB * 16 * 7 / 2 + NSM - 1) / NSM;
             __builtin_amdgcn_sched_group_barrier(0x100, GQA_PF_K, 0);
@@ -468,7 +581,9 @@ fwd_bf16_kernel(FwdParams p) {
         l_run += l_tile;
         accumulate(vf, pf);
         mask(t + 1, s_nxt);
-        if (!tail) {
+        if constexpr (F8) {
+            barrier_keep2_f8();
+        } else if (!tail) {
             barrier_keep2();
         } else {
             // loads issued after K(t+2) and V(t+1): K(t+3) and V(t+2) (by the
@@ -494,7 +609,8 @@ fwd_bf16_kernel(FwdParams p) {
     // ---- epilogue: one division by l, L = m + log(l) ----
     const float l_tot = pair_sum32(l_run);
     const bool empty = !(l_tot > 0.f);
-    const float inv = empty ? 0.f : 1.f / l_tot;
+    float inv = empty ? 0.f : 1.f / l_tot;
+    if constexpr (F8) inv *= p.o_scale;
     // O leaves through this wave's own 32 rows of Qs (its Q fragment was read
     // from there before the loop; no other wave touches them): lane (col, half)
     // writes its 8-byte pieces of row col, then every lane reads whole 16-byte
@@ -534,10 +650,10 @@ fwd_bf16_kernel(FwdParams p) {
     }
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, bool F8>
 hipError_t launch_t(const FwdParams &p, hipStream_t s) {
     const long long grid = (long long)p.n_hg * p.n_rb;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN, F8>), dim3((unsigned)grid),
                        dim3(Waves<D>::NTHREADS), 0,
                        s, p);
     return hipGetLastError();
@@ -549,7 +665,22 @@ int fwd_bf16_rows_per_tile(int d) { return d == 128 ? Waves<128>::BM : Waves<64>
 
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, bool causal, bool varlen, hipStream_t s) {
 #define GQA_CASE(D_, C_, V_) \
-    if (d == D_ && causal == C_ && varlen == V_) return launch_t<D_, C_, V_>(p, s);
+    if (d == D_ && causal == C_ && varlen == V_) return launch_t<D_, C_, V_, false>(p, s);
+    GQA_CASE(64, false, false)
+    GQA_CASE(64, true, false)
+    GQA_CASE(64, false, true)
+    GQA_CASE(64, true, true)
+    GQA_CASE(128, false, false)
+    GQA_CASE(128, true, false)
+    GQA_CASE(128, false, true)
+    GQA_CASE(128, true, true)
+#undef GQA_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_fp8(const FwdParams &p, int d, bool causal, bool varlen, hipStream_t s) {
+#define GQA_CASE(D_, C_, V_) \
+    if (d == D_ && causal == C_ && varlen == V_) return launch_t<D_, C_, V_, true>(p, s);
     GQA_CASE(64, false, false)
     GQA_CASE(64, true, false)
     GQA_CASE(64, false, true)

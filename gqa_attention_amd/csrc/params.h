@@ -22,7 +22,8 @@ struct FwdParams {
     int n_hg;                    // B * Hq / gpack
     int n_rb;                    // row tiles per head group
     float scale;                 // softmax scale (> 0)
-    float scale_log2;            // scale * log2(e)
+    float scale_log2;            // scale * log2(e) (* q_scale * k_scale for fp8 inputs)
+    float o_scale;               // fp8 inputs: V dequantisation scale applied to O (else 1)
     // split-KV partial mode (fp32 kernel only, Sq == 1): key range of split s
     // is [s * split_chunk, (s + 1) * split_chunk); partials go to ws_o / ws_lse.
     int num_splits;
@@ -83,6 +84,7 @@ struct BwdParams {
 
 // Launchers (one per kernel family). Each returns a hipError_t.
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, bool causal, bool varlen, hipStream_t s);
+hipError_t launch_fwd_fp8(const FwdParams &p, int d, bool causal, bool varlen, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdParams &p, int d, bool causal, bool varlen, bool split,
                           hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeParams &p, int d, bool paged, bool fp8_kv, hipStream_t s);

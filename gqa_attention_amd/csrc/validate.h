@@ -149,6 +149,9 @@ inline int validate_bwd(const void *q, const void *k, const void *v, const void 
 
 inline bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// A per-tensor dequantisation scale: finite and > 0.
+inline bool valid_dequant_scale(float s) { return std::isfinite(s) && s > 0.f; }
+
 inline int validate_decode_ex(const void *q, const void *kc, const void *vc, const void *out,
                               const float *lse, int B, int Hq, int Hkv, int d, float scale,
                               const int32_t *seqlens, int max_seqlen_k, const int32_t *table,

@@ -50,6 +50,9 @@ class Workload:
     max_seqlen_q: Optional[int] = None
     max_seqlen_k: Optional[int] = None
     decode: bool = False
+    # fp8 e4m3 inputs (q, k, v are torch.float8_e4m3fn): (q_scale, k_scale,
+    # v_scale), the per-tensor dequantisation scales; None for bf16 / fp32.
+    fp8_scales: Optional[tuple] = None
 
     @property
     def varlen(self) -> bool:
@@ -86,6 +89,29 @@ def varlen(lengths_q, lengths_k, Hq: int, Hkv: int, d: int, *, seed: int,
     ck = torch.tensor([0] + lk, dtype=torch.int64).cumsum(0).to(torch.int32)
     return Workload(name, q, k, v, causal, d ** -0.5 if scale is None else scale,
                     cq, ck, max(lq) if lq else 0, max(lk) if lk else 0)
+
+
+def fixed_fp8(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int, *, seed: int,
+              causal: bool = False, q_scale: float = 1.0, k_scale: float = 1.0,
+              v_scale: float = 1.0, scale: Optional[float] = None,
+              name: str = "fixed_fp8") -> Workload:
+    """As ``fixed``, with the N(0, 1) draws rounded to e4m3
+    (``.to(torch.float8_e4m3fn)``) and the given dequantisation scales."""
+    w = fixed(B, Hq, Hkv, Sq, Sk, d, seed=seed, dtype=torch.float8_e4m3fn, causal=causal,
+              scale=scale, name=name)
+    w.fp8_scales = (float(q_scale), float(k_scale), float(v_scale))
+    return w
+
+
+def varlen_fp8(lengths_q, lengths_k, Hq: int, Hkv: int, d: int, *, seed: int,
+               causal: bool = False, q_scale: float = 1.0, k_scale: float = 1.0,
+               v_scale: float = 1.0, scale: Optional[float] = None,
+               name: str = "varlen_fp8") -> Workload:
+    """As ``varlen``, with e4m3 storage and dequantisation scales."""
+    w = varlen(lengths_q, lengths_k, Hq, Hkv, d, seed=seed, dtype=torch.float8_e4m3fn,
+               causal=causal, scale=scale, name=name)
+    w.fp8_scales = (float(q_scale), float(k_scale), float(v_scale))
+    return w
 
 
 def decode(B: int, Hq: int, Hkv: int, Sk: int, d: int, *, seed: int,
@@ -249,6 +275,20 @@ def varlen_packed_causal_48_12() -> Workload:
                     128 ** -0.5, cu, cu.clone(), max(lengths), max(lengths))
 
 
+def llama31_8b_prefill_fp8() -> Workload:
+    """The Llama 3.1 8B causal prefill shape (B 1, S 8192, 32 / 8 heads, d 128)
+    over e4m3 inputs with q_scale 0.5, k_scale 0.25, v_scale 0.5 (seed 10)."""
+    return fixed_fp8(1, 32, 8, 8192, 8192, 128, seed=10, causal=True, q_scale=0.5,
+                     k_scale=0.25, v_scale=0.5, name="llama31_8b_prefill_fp8_s8192_h32_kv8_d128")
+
+
+def bert_base_encoder_fp8() -> Workload:
+    """The BERT-base encoder shape (B 64, S 512, 12 heads, d 64, non-causal)
+    over e4m3 inputs with q_scale 0.5, k_scale 0.25, v_scale 0.5 (seed 11)."""
+    return fixed_fp8(64, 12, 12, 512, 512, 64, seed=11, causal=False, q_scale=0.5,
+                     k_scale=0.25, v_scale=0.5, name="bert_base_encoder_fp8_b64_s512_h12_d64")
+
+
 def llama31_8b_decode_ragged_paged(fp8: bool = False) -> CacheWorkload:
     """Decode over a paged cache of ragged lengths: B 64, 32 query / 8 KV
     heads, d 128, cache lengths uniform on [1, 8192] (drawn first from seed 6),
@@ -284,4 +324,6 @@ NAMED = {
     "llama31_8b_prefill": llama31_8b_prefill,
     "llama31_8b_decode": llama31_8b_decode,
     "varlen_packed_causal": varlen_packed_causal_48_12,
+    "llama31_8b_prefill_fp8": llama31_8b_prefill_fp8,
+    "bert_base_encoder_fp8": bert_base_encoder_fp8,
 }

@@ -56,7 +56,8 @@ extern "C" {
 typedef enum {
     GQA_DTYPE_BF16 = 0,
     GQA_DTYPE_FP32 = 1,
-    GQA_DTYPE_FP8_E4M3 = 2  /* K/V cache of gqa_attn_decode_ex only (OCP e4m3, 1 byte) */
+    GQA_DTYPE_FP8_E4M3 = 2  /* K/V cache of gqa_attn_decode_ex (OCP e4m3, 1 byte); the inputs
+                               of gqa_attn_fwd_fp8 have this format implicitly */
 } gqa_dtype;
 
 enum {
@@ -91,6 +92,33 @@ int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *
                  int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
                  const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
                  int dtype, void *stream);
+
+/*
+ * gqa_attn_fwd_fp8 - gqa_attn_fwd over fp8 e4m3 inputs (the gitcode GQA
+ * batch-size guide's hardware section: FP8 precision to relieve memory
+ * bandwidth; its parameter table's precision row). The pages fix no format;
+ * the OCP E4M3 byte format is used with one dequantisation scale per tensor:
+ * the value of a stored code x is decode(x) * q_scale (resp. k_scale,
+ * v_scale).
+ *
+ * q, k, v: e4m3 codes (1 byte each), in the layouts of gqa_attn_fwd (fixed
+ *   or variable length, same cu_seqlens rules); out: bf16 in q's layout;
+ *   lse: fp32 as for gqa_attn_fwd.
+ * Result: the attention of the dequantised tensors, with the softmax scale
+ *   `scale`, computed as follows: scores on the fp8 matrix cores (exact
+ *   products of the codes summed in fp32, then multiplied by scale x q_scale
+ *   x k_scale), probabilities rounded to bf16, V widened exactly to bf16 for
+ *   the bf16 matrix-core product, O multiplied by v_scale before the final
+ *   rounding to bf16. Rounding is that of gqa_attn_fwd in bf16 mode.
+ * Requirements: those of gqa_attn_fwd; q_scale, k_scale, v_scale finite and
+ *   > 0, and scale x q_scale x k_scale finite and > 0. Codes 0x7f / 0xff
+ *   (NaN) give undefined results.
+ * Errors: GQA_EINVAL, GQA_EUNSUPPORTED (d not in {64, 128}), GQA_ELAUNCH.
+ */
+int gqa_attn_fwd_fp8(const void *q, const void *k, const void *v, void *out, float *lse,
+                     int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,
+                     const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, float q_scale,
+                     float k_scale, float v_scale, void *stream);
 
 /*
  * gqa_attn_bwd_workspace_bytes - size of the caller-owned workspace of

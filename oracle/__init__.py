@@ -11,6 +11,7 @@ Modules:
   cache      decode over a general cache: per-sequence lengths, pages, a
              sliding window, fp8 (e4m3) storage
   backward   gradients dq, dk, dv of the definition (chain rule, materialised)
+  fp8_forward  the definition over fp8 (e4m3) inputs with per-tensor scales
 """
 from .gqa import (attention, attention_rows, decode, decode_partials,  # noqa: F401
                         merge_partials, split_ranges, attention_flops, head_rows,
@@ -18,3 +19,4 @@ from .gqa import (attention, attention_rows, decode, decode_partials,  # noqa: F
 from .kv_cache import kv_cache_bytes, kv_cache_elements  # noqa: F401
 from .cache import decode_cache, fp8_e4m3_decode  # noqa: F401
 from .backward import attention_grad, attention_grad_flops  # noqa: F401
+from .fp8_forward import attention_fp8, attention_rows_fp8  # noqa: F401

@@ -34,7 +34,7 @@ def test_header_declares_the_api():
                                     "gqa_attn_decode", "gqa_attn_decode_ex",
                                     "gqa_attn_decode_num_splits",
                                     "gqa_attn_decode_workspace_bytes", "gqa_attn_fwd",
-                                    "gqa_attn_strerror"]
+                                    "gqa_attn_fwd_fp8", "gqa_attn_strerror"]
 
 
 @needs_lib
@@ -109,6 +109,43 @@ def test_fwd_argument_errors(kw, code):
 def test_fwd_varlen_without_rows_is_a_noop():
     # variable length with max_seqlen_q == 0: nothing to compute, nothing launched
     assert fwd_call(cu_q=FAKE, cu_k=FAKE, Sq=0, Sk=0) == ga.GQA_OK
+
+
+def fwd8_call(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, B=1, Hq=8, Hkv=2, Sq=16, Sk=16, d=64,
+             scale=0.125, causal=1, cu_q=None, cu_k=None, qs=0.5, ks=0.25, vs=2.0, stream=None)
+    a.update(kw)
+    return ga.lib().gqa_attn_fwd_fp8(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"],
+                                     a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["d"], a["scale"],
+                                     a["causal"], a["cu_q"], a["cu_k"], a["qs"], a["ks"], a["vs"],
+                                     a["stream"])
+
+
+FWD8_ERRORS = [
+    (dict(q=None), ga.GQA_EINVAL),
+    (dict(d=96), ga.GQA_EUNSUPPORTED),
+    (dict(Hq=6, Hkv=4), ga.GQA_EINVAL),
+    (dict(Sq=0), ga.GQA_EINVAL),
+    (dict(scale=0.0), ga.GQA_EINVAL),
+    (dict(qs=0.0), ga.GQA_EINVAL),
+    (dict(ks=-1.0), ga.GQA_EINVAL),
+    (dict(vs=float("nan")), ga.GQA_EINVAL),
+    (dict(qs=float("inf")), ga.GQA_EINVAL),
+    (dict(scale=1e30, qs=1e30, ks=1e30), ga.GQA_EINVAL),  # combined score scale overflows
+    (dict(cu_q=FAKE), ga.GQA_EINVAL),
+    (dict(k=FAKE + 8), ga.GQA_EINVAL),
+]
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,code", FWD8_ERRORS, ids=lambda x: str(x))
+def test_fwd_fp8_argument_errors(kw, code):
+    assert fwd8_call(**kw) == code
+
+
+@needs_lib
+def test_fwd_fp8_varlen_without_rows_is_a_noop():
+    assert fwd8_call(cu_q=FAKE, cu_k=FAKE, Sq=0, Sk=0) == ga.GQA_OK
 
 
 DEC_ERRORS = [
