@@ -13,7 +13,8 @@ launch stream), the CPU oracle timed on a bounded sample (rank 0, N = 1) and,
 under "extra", the other workloads (8192-token causal GQA prefill, split-KV
 decode at num_splits 1/2/4/8, packed variable-length causal GQA, tiny fp32,
 the backward pass on the encoder, prefill and varlen workloads, and decode over
-general caches: ragged paged bf16 and fp8, sliding window).
+general caches: ragged paged bf16 and fp8, sliding window; the fp8-input
+forward on the prefill and encoder shapes).
 
 Flop count: 4 * d per visible (query, key) pair per query head (two products,
 multiply-add = 2 flops); the backward counts 10 * d (five products). Decode bytes: the K and V cache bytes read,
@@ -36,6 +37,11 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector peak (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published)
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix peak (published)
+# The fp8-input forward runs half of its algorithmic flops (S = Q K^T) on the
+# fp8 matrix cores and half (O = P V, P in bf16) on the bf16 ones: its peak is
+# the rate at which that mix could run, 1 / (0.5 / 5000 + 0.5 / 2500).
+PEAK_FP8_FWD_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 METRIC = "fwd attention TFLOP/s (% MFMA peak); decode KV GB/s (% HBM peak)"
 
 
@@ -72,6 +78,7 @@ def source_digest(files) -> str:
 
 KERNEL_SOURCES = {
     "fwd_bf16": ["gqa_attention_amd/csrc/fwd_bf16.hip", "gqa_attention_amd/csrc/device_util.h"],
+    "fwd_fp8": ["gqa_attention_amd/csrc/fwd_bf16.hip", "gqa_attention_amd/csrc/device_util.h"],
     "decode_bf16": ["gqa_attention_amd/csrc/decode_bf16.hip",
                     "gqa_attention_amd/csrc/device_util.h"],
 }
@@ -149,7 +156,8 @@ def bench_fwd(torch, ga, w, steps, warmup, sets, **warm):
     dev_sets = to_device(torch, w, sets)
     cq = w.cu_seqlens_q.cuda() if w.varlen else None
     ck = w.cu_seqlens_k.cuda() if w.varlen else None
-    outs = [(torch.empty_like(q), None) for q, _, _ in dev_sets]
+    out_dt = torch.bfloat16 if w.fp8_scales is not None else w.q.dtype
+    outs = [(torch.empty(q.shape, dtype=out_dt, device="cuda"), None) for q, _, _ in dev_sets]
     lses = []
     for q, _, _ in dev_sets:
         shape = (q.shape[0], q.shape[1]) if w.varlen else (q.shape[0], q.shape[2], q.shape[1])
@@ -162,10 +170,11 @@ def bench_fwd(torch, ga, w, steps, warmup, sets, **warm):
         if w.varlen:
             plans.append(ga.FwdPlan(q, k, v, causal=w.causal, scale=w.scale, cu_seqlens_q=cq,
                                     cu_seqlens_k=ck, max_seqlen_q=w.max_seqlen_q,
-                                    max_seqlen_k=w.max_seqlen_k, out=outs[j][0], lse=lses[j]))
+                                    max_seqlen_k=w.max_seqlen_k, out=outs[j][0], lse=lses[j],
+                                    fp8_scales=w.fp8_scales))
         else:
             plans.append(ga.FwdPlan(q, k, v, causal=w.causal, scale=w.scale, out=outs[j][0],
-                                    lse=lses[j]))
+                                    lse=lses[j], fp8_scales=w.fp8_scales))
 
     def step(i):
         plans[i % sets].run()
@@ -265,8 +274,12 @@ def cpu_baseline(w, budget_s=15.0):
     done, flops = 0, 0
     t0 = time.perf_counter()
     while done < B and (time.perf_counter() - t0) < budget_s:
-        oracle.attention(w.q[done:done + 1], w.k[done:done + 1], w.v[done:done + 1], w.scale,
-                         w.causal)
+        if w.fp8_scales is not None:
+            oracle.attention_fp8(w.q[done:done + 1], w.k[done:done + 1], w.v[done:done + 1],
+                                 w.scale, w.causal, *w.fp8_scales)
+        else:
+            oracle.attention(w.q[done:done + 1], w.k[done:done + 1], w.v[done:done + 1],
+                             w.scale, w.causal)
         flops += fwd_flops(w.q.shape[1], w.k.shape[1], w.q.shape[2], w.q.shape[3], w.causal)
         done += 1
     el = time.perf_counter() - t0
@@ -316,6 +329,9 @@ def summarize_counters(pmc_dir: str, out_path: str) -> dict:
         f, w = read(wl + "_fetch"), read(wl + "_write")
         for kname, vals in f.items():
             tag = next((v for k, v in kernels.items() if k in kname), None)
+            # the forward's fp8-input instances: fwd_bf16_kernel<D, causal, varlen, true>
+            if tag == "fwd_bf16" and kname.split(">")[0].replace(" ", "").endswith(",true"):
+                tag = "fwd_fp8"
             if tag is None or kname not in w:
                 continue
             fb = statistics.mean(vals) * 1024 * scale_fetch
@@ -332,6 +348,8 @@ def summarize_counters(pmc_dir: str, out_path: str) -> dict:
 
 
 WORKLOAD_NAMES = {
+    "llama31_8b_prefill_fp8": "llama31_8b_prefill_fp8_s8192_h32_kv8_d128",
+    "bert_base_encoder_fp8": "bert_base_encoder_fp8_b64_s512_h12_d64",
     "bert_base_encoder": "bert_base_encoder_b64_s512_h12_d64",
     "llama31_8b_prefill": "llama31_8b_prefill_s8192_h32_kv8_d128",
     "llama31_8b_decode": "llama31_8b_decode_b64_kv4096_h32_kv8_d128",
@@ -351,7 +369,8 @@ def main():
                     choices=["bert_base_encoder", "llama31_8b_prefill", "llama31_8b_decode",
                              "varlen_packed_causal", "tiny_causal_gqa_fp32",
                              "decode_ragged_paged", "decode_ragged_paged_fp8",
-                             "decode_sliding_window"])
+                             "decode_sliding_window", "llama31_8b_prefill_fp8",
+                             "bert_base_encoder_fp8"])
     ap.add_argument("--num-splits", type=int, default=1, help="decode workload only")
     ap.add_argument("--pass", dest="pass_", choices=["forward", "backward"], default="forward",
                     help="backward: time gqa_attn_bwd on a forward workload (prints that line only)")
@@ -385,12 +404,20 @@ def main():
     # about 20 ms of launches
     ramp = dict(warm_seconds=0.05, timed_seconds=0.02)
 
+    def fwd_kind(w):
+        """(kernel, dtype label, peak TFLOP/s, bound) of a forward workload."""
+        if w.fp8_scales is not None:
+            return "fwd_fp8", "fp8_e4m3", PEAK_FP8_FWD_TFLOPS, "mfma"
+        if w.q.dtype == torch.bfloat16:
+            return "fwd_bf16", "bf16", PEAK_BF16_TFLOPS, "mfma"
+        return "fwd_f32", "f32", PEAK_FP32_TFLOPS, "alu"
+
     def fwd_entry(name, w, steps, warmup, sets, **warm):
         r = bench_fwd(torch, ga, w, steps, warmup, sets, **warm)
         tf = r["flops"] / (r["avg_ms"] * 1e-3) / 1e12
-        peak = PEAK_BF16_TFLOPS if w.q.dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
-        return r, {"workload": w.name, "kernel": "fwd_bf16" if w.q.dtype == torch.bfloat16
-                   else "fwd_f32", "tflops": round(tf, 2), "frac_peak": round(tf / peak, 4),
+        kernel, _, peak, _ = fwd_kind(w)
+        return r, {"workload": w.name, "kernel": kernel, "tflops": round(tf, 2),
+                   "peak": round(peak, 1), "frac_peak": round(tf / peak, 4),
                    "ms_per_launch": round(r["avg_ms"], 5),
                    "gflop": round(r["flops"] / 1e9, 3)}
 
@@ -400,8 +427,10 @@ def main():
         "varlen_packed_causal": gqa_inputs.varlen_packed_causal_48_12,
         "tiny_causal_gqa_fp32": gqa_inputs.tiny_causal_gqa_fp32,
         "llama31_8b_decode": gqa_inputs.llama31_8b_decode,
+        "llama31_8b_prefill_fp8": gqa_inputs.llama31_8b_prefill_fp8,
+        "bert_base_encoder_fp8": gqa_inputs.bert_base_encoder_fp8,
     }
-    sets_for = {"bert_base_encoder": 3, "llama31_8b_decode": 2}
+    sets_for = {"bert_base_encoder": 3, "bert_base_encoder_fp8": 3, "llama31_8b_decode": 2}
 
     def cache_entry(wc, ns, steps, warmup, **warm):
         rc = bench_decode_ex(torch, ga, wc, ns, steps, warmup, **warm)
@@ -413,7 +442,7 @@ def main():
 
     if args.pass_ == "backward":
         w = loaders[args.workload]()
-        if w.decode or w.q.dtype != torch.bfloat16:
+        if w.decode or w.q.dtype != torch.bfloat16 or w.fp8_scales is not None:
             print("the backward pass is timed on the bf16 forward workloads", file=sys.stderr)
             sys.exit(2)
         r = bench_bwd(torch, ga, w, args.steps, args.warmup)
@@ -470,13 +499,10 @@ def main():
         tf = r["flops"] / (r["avg_ms"] * 1e-3) / 1e12
         value = r["flops"] * args.steps / r["wall"] / 1e12
         unit = "TFLOP/s"
-        bf16 = w.q.dtype == torch.bfloat16
-        dtype_s = "bf16" if bf16 else "f32"
-        kernel = "fwd_bf16" if bf16 else "fwd_f32"
-        peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_TFLOPS
-        roof = {"bound": "mfma" if bf16 else "alu", "achieved": round(tf, 2), "peak": peak,
+        kernel, dtype_s, peak, bound = fwd_kind(w)
+        roof = {"bound": bound, "achieved": round(tf, 2), "peak": round(peak, 1),
                 "unit": "TFLOP/s", "frac": round(tf / peak, 4)}
-        traffic = measured_traffic(kernel, w.name) if bf16 else None
+        traffic = measured_traffic(kernel, w.name) if bound == "mfma" else None
         if w.varlen:
             config = {"workload": w.name, "sequences": len(w.cu_seqlens_q) - 1,
                       "total_tokens": w.q.shape[0], "Hq": w.q.shape[1], "Hkv": w.k.shape[1],
@@ -500,7 +526,7 @@ def main():
     if not args.no_extra:
         extra = []
         for name in ["llama31_8b_prefill", "varlen_packed_causal", "tiny_causal_gqa_fp32",
-                     "bert_base_encoder"]:
+                     "bert_base_encoder", "llama31_8b_prefill_fp8", "bert_base_encoder_fp8"]:
             if name == args.workload:
                 continue
             wx = loaders[name]()
