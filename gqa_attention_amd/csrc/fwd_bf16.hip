@@ -159,6 +159,13 @@ fwd_bf16_kernel(FwdParams p) {
         const int slot = pid >> 3;
         hg = (slot / p.n_rb) * 8 + (pid & 7);
         rank = slot % p.n_rb;
+        if constexpr (F8 && D == 64) {
+            // A 64-byte fp8 row fills half of a 128-byte line whose other
+            // half is the same token's row of the next head group: XCD x
+            // runs head groups 16 a + 2 x and 16 a + 2 x + 1 at the same
+            // time, so both halves of each line are used from its L2.
+            if ((p.n_hg & 15) == 0) hg = (hg >> 4) * 16 + (hg & 7) * 2 + ((hg >> 3) & 1);
+        }
     } else {
         hg = pid / p.n_rb;
         rank = pid % p.n_rb;

@@ -54,6 +54,10 @@ FIXED = [
     (1, 8, 1, 1, 333, False, (0.5, 0.25, 0.5)),     # a single query row
     (1, 16, 2, 33, 1, False, (0.5, 0.25, 0.5)),     # a single key
     (1, 32, 8, 700, 700, True, (0.5, 0.25, 0.5)),   # Llama heads, several 256-row tiles
+    # head-group counts that are multiples of 16 (d = 64 pairs adjacent head
+    # groups on one XCD)
+    (2, 16, 16, 200, 200, False, (0.5, 0.25, 0.5)),
+    (2, 32, 8, 150, 170, True, (0.5, 0.25, 0.5)),
 ]
 
 

@@ -11,6 +11,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 import gqa_attention_amd as ga
 
@@ -141,6 +142,12 @@ FWD8_ERRORS = [
 @pytest.mark.parametrize("kw,code", FWD8_ERRORS, ids=lambda x: str(x))
 def test_fwd_fp8_argument_errors(kw, code):
     assert fwd8_call(**kw) == code
+
+
+def test_python_fwd_fp8_rejects_other_dtypes():
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="float8_e4m3fn"):
+        ga.fwd_fp8(q, q, q)
 
 
 @needs_lib
