@@ -1,4 +1,6 @@
-// Fused GQA attention forward, bf16 in / bf16 out, on gfx950 matrix cores.
+// Fused GQA attention forward, bf16 in / bf16 out, on gfx950 matrix cores;
+// the same kernel with its F8 flag set serves fp8 e4m3 inputs (see the note
+// above the kernel template).
 //
 // Method (FlashAttention-2 summary, azimuth.plus): the query rows are cut into
 // independent row tiles, one workgroup each (sequence-length parallelism);
