@@ -222,6 +222,19 @@ def test_num_splits_agree():
         assert (l - outs[0][1]).abs().max().item() <= 1e-3
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_many_sequences(causal):
+    """More sequences than the longest-first ranking covers (70 > 64), and a
+    ranked batch of 64 with equal lengths among them (ties by index)."""
+    g = torch.Generator().manual_seed(31)
+    for n in (70, 64):
+        lens = torch.randint(0, 90, (n,), generator=g).tolist()
+        lens[5] = lens[9] = lens[40] = 77
+        w = gqa_inputs.varlen(lens, lens, 8, 2, 64, seed=32 + n, causal=causal)
+        o, l = run_fwd(w)
+        compare(o, l, *oracle_fwd(w), torch.bfloat16, f"varlen {n} sequences")
+
+
 def test_empty_varlen_batch():
     w = gqa_inputs.varlen([0, 0], [0, 5], 4, 2, 64, seed=13)
     o, l = ga.fwd(w.q.cuda(), w.k.cuda(), w.v.cuda(), cu_seqlens_q=w.cu_seqlens_q.cuda(),
