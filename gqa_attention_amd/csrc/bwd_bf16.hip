@@ -170,7 +170,16 @@ bwd_dkdv_kernel(BwdParams p) {
         grp = pid / n_inner;
         inner = pid % n_inner;
     }
-    const int b = grp / p.Hkv, kvh = grp - b * p.Hkv;
+    const int kvh = grp % p.Hkv;
+    int b = grp / p.Hkv;
+    if constexpr (VARLEN) {
+        // longest first, as the forward; grp follows the sequence taken (the
+        // row-chunk partials and their reduction are indexed by it)
+        if (p.B > 1 && p.B <= kLptMax) {
+            b = lpt_sequence(p.cu_q, p.cu_k, p.B, b, tid);
+            grp = b * p.Hkv + kvh;
+        }
+    }
     // Paired mode (causal, unchunked): key block i and its mirror
     // n_kb(b) - 1 - i, one after the other, so that every workgroup walks
     // about the same number of rows (the first block sees the most rows,
@@ -572,7 +581,11 @@ bwd_dq_kernel(BwdParams p) {
         rank = pid % p.n_rb;
     }
     const int rb = CAUSAL ? (p.n_rb - 1 - rank) : rank;
-    const int b = hg / p.Hkv, kvh = hg - b * p.Hkv;
+    const int kvh = hg % p.Hkv;
+    int b = hg / p.Hkv;
+    if constexpr (VARLEN) {
+        if (p.B > 1 && p.B <= kLptMax) b = lpt_sequence(p.cu_q, p.cu_k, p.B, b, tid);  // longest first
+    }
     const int G = p.G, qh0 = kvh * G;
     int q_tok0 = b * p.Sq, Lq = p.Sq, k_tok0 = b * p.Sk, Lk = p.Sk;
     if (VARLEN) {

@@ -102,6 +102,32 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // 2^x on the transcendental unit (v_exp_f32); exact 0 for -inf.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Longest first over the sequences of a packed batch (prefix offsets cu_q,
+// cu_k, B <= kLptMax <= threads per workgroup): returns the index of the
+// sequence whose work Lq x Lk ranks r-th largest (ties by index). Workgroups
+// start roughly in blockIdx order, so giving rank r to the r-th group of
+// workgroups starts the heaviest pieces first. Every thread of the workgroup
+// must call it (two barriers).
+constexpr int kLptMax = 64;
+__device__ __forceinline__ int lpt_sequence(const int32_t *cu_q, const int32_t *cu_k, int B, int r,
+                                            int tid) {
+    __shared__ long long s_work[kLptMax];
+    __shared__ int s_pick;
+    if (tid < B) s_work[tid] = (long long)(cu_q[tid + 1] - cu_q[tid]) * (cu_k[tid + 1] - cu_k[tid]);
+    __syncthreads();
+    if (tid < B) {
+        const long long mine = s_work[tid];
+        int rank = 0;
+        for (int y = 0; y < B; ++y) {
+            const long long o = s_work[y];
+            rank += (o > mine) || (o == mine && y < tid);
+        }
+        if (rank == r) s_pick = tid;
+    }
+    __syncthreads();
+    return s_pick;
+}
+
 // fp8 e4m3 -> bf16 (exact: every e4m3 value is a bf16 value) for 4 packed
 // values.
 __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {

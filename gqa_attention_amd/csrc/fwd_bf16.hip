@@ -64,10 +64,6 @@ namespace {
 #define GQA_VR_DIV 1
 #endif
 
-// Variable-length batches of at most this many sequences are scheduled
-// longest first (one thread ranks one sequence).
-constexpr int kVarlenLptMax = 64;
-
 // Wavefronts per workgroup (32 query rows each): 8 at d = 128, where sharing
 // each K/V tile among 256 rows measured 3-5 % faster than 128 rows, 4 at
 // d = 64, where 8 waves measured 15 % slower on the encoder workload.
@@ -181,29 +177,10 @@ fwd_bf16_kernel(FwdParams p) {
     const int seq_rank = hg / hpb;
     const int qh0 = (hg - seq_rank * hpb) * p.gpack;
     int b = seq_rank;
+    // Longest first (packed batches of 2 .. kLptMax sequences): the heaviest
+    // row tiles start first and short sequences fill the tail.
     if constexpr (VARLEN) {
-        // Longest first: workgroups start roughly in blockIdx order, so the
-        // sequence with the r-th largest Lq x Lk (ties by index) takes the
-        // r-th group of head groups; the heaviest row tiles start first and
-        // short sequences fill the tail.
-        if (p.B > 1 && p.B <= kVarlenLptMax) {
-            __shared__ long long s_work[kVarlenLptMax];
-            __shared__ int s_pick;
-            if (tid < p.B)
-                s_work[tid] = (long long)(p.cu_q[tid + 1] - p.cu_q[tid]) * (p.cu_k[tid + 1] - p.cu_k[tid]);
-            __syncthreads();
-            if (tid < p.B) {
-                const long long mine = s_work[tid];
-                int r = 0;
-                for (int y = 0; y < p.B; ++y) {
-                    const long long o = s_work[y];
-                    r += (o > mine) || (o == mine && y < tid);
-                }
-                if (r == seq_rank) s_pick = tid;
-            }
-            __syncthreads();
-            b = s_pick;
-        }
+        if (p.B > 1 && p.B <= kLptMax) b = lpt_sequence(p.cu_q, p.cu_k, p.B, seq_rank, tid);
     }
     const int kvh = qh0 / p.G;
 
