@@ -36,7 +36,7 @@ from typing import Optional, Tuple
 
 import torch
 
-__all__ = ["fwd", "bwd", "decode", "decode_ex", "FwdPlan", "BwdPlan", "DecodePlan", "DecodeExPlan",
+__all__ = ["fwd", "fwd_fp8", "bwd", "decode", "decode_ex", "FwdPlan", "BwdPlan", "DecodePlan", "DecodeExPlan",
            "bwd_workspace_bytes",
            "decode_workspace_bytes", "decode_num_splits", "strerror", "lib", "library_path",
            "GQA_OK", "GQA_EINVAL", "GQA_EUNSUPPORTED", "GQA_EWORKSPACE", "GQA_ELAUNCH",
