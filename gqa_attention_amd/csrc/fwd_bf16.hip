@@ -104,8 +104,9 @@ struct Cfg {
 
 // F8: q, k, v hold fp8 e4m3 codes (one byte each) with per-tensor
 // dequantisation scales folded into scale_log2 (q_scale k_scale) and o_scale
-// (v_scale). The scores run on the fp8 matrix cores (32x32x64, exact products
-// summed in fp32). K and V tiles arrive together, one 16-byte direct load per
+// (v_scale). The scores run on the fp8 matrix cores (32x32x64: exact
+// products; each group of 64 is summed inside the matrix core at somewhat
+// less than fp32 precision, then accumulated in fp32). K and V tiles arrive together, one 16-byte direct load per
 // wave (half of the waves fetch K rows, half V rows), into one ring slot: K in
 // its lower half (fp8 rows, swizzled for the operand reads), V in its upper
 // half (unswizzled). One step before its use, the workgroup widens the V tile

@@ -106,10 +106,12 @@ int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *
  *   lse: fp32 as for gqa_attn_fwd.
  * Result: the attention of the dequantised tensors, with the softmax scale
  *   `scale`, computed as follows: scores on the fp8 matrix cores (exact
- *   products of the codes summed in fp32, then multiplied by scale x q_scale
- *   x k_scale), probabilities rounded to bf16, V widened exactly to bf16 for
- *   the bf16 matrix-core product, O multiplied by v_scale before the final
- *   rounding to bf16. Rounding is that of gqa_attn_fwd in bf16 mode.
+ *   products of the codes; each sum of 64 of them is formed inside the
+ *   matrix core at somewhat less than fp32 precision, measured at about
+ *   2^-15 of the score, then accumulated in fp32 and multiplied by scale x
+ *   q_scale x k_scale), probabilities rounded to bf16, V widened exactly to
+ *   bf16 for the bf16 matrix-core product, O multiplied by v_scale before the
+ *   final rounding to bf16.
  * Requirements: those of gqa_attn_fwd; q_scale, k_scale, v_scale finite and
  *   > 0, and scale x q_scale x k_scale finite and > 0. Codes 0x7f / 0xff
  *   (NaN) give undefined results.
