@@ -41,23 +41,23 @@ def test_fwd_at_max_row_pitch(hkv, d):
     compare(got_o, got_l, ro, rl, torch.bfloat16, f"fwd max pitch hkv={hkv} d={d}")
 
 
-def test_fwd_fp8_at_max_row_pitch():
-    hkv, d = 32768, 128
-    w = gi.fixed_fp8(1, hkv, hkv, S, S, d, seed=62, causal=False, q_scale=0.5, k_scale=0.25,
-                     v_scale=0.5)
+@pytest.mark.parametrize("hkv,d,causal", [(32768, 128, False), (65536, 64, True)])
+def test_fwd_fp8_at_max_row_pitch(hkv, d, causal):
+    w = gi.fixed_fp8(1, hkv, hkv, S, S, d, seed=62 + d, causal=causal, q_scale=0.5,
+                     k_scale=0.25, v_scale=0.5)
     o, l = ga.fwd_fp8(w.q.cuda(), w.k.cuda(), w.v.cuda(), q_scale=0.5, k_scale=0.25,
-                      v_scale=0.5, causal=False, scale=w.scale)
+                      v_scale=0.5, causal=causal, scale=w.scale)
     torch.cuda.synchronize()
     rows = _rows(torch.Generator().manual_seed(63), 24, S, hkv)
-    ro, rl = of8.attention_rows_fp8(w.q, w.k, w.v, w.scale, False, 0.5, 0.25, 0.5, rows)
+    ro, rl = of8.attention_rows_fp8(w.q, w.k, w.v, w.scale, causal, 0.5, 0.25, 0.5, rows)
     got_o = torch.stack([o[b, i, h].cpu() for b, i, h in rows])
     got_l = torch.tensor([float(l[b, h, i]) for b, i, h in rows])
     compare(got_o, got_l, ro, rl, torch.bfloat16, "fwd fp8 max pitch")
 
 
-def test_bwd_at_max_row_pitch():
-    hkv, d = 32768, 128
-    w = gi.fixed(1, hkv, hkv, S, S, d, seed=64, causal=True)
+@pytest.mark.parametrize("hkv,d", [(32768, 128), (65536, 64)])
+def test_bwd_at_max_row_pitch(hkv, d):
+    w = gi.fixed(1, hkv, hkv, S, S, d, seed=64 + d, causal=True)
     g = torch.Generator().manual_seed(65)
     do = torch.randn(w.q.shape, generator=g).to(torch.bfloat16)
     q, k, v = w.q.cuda(), w.k.cuda(), w.v.cuda()
