@@ -193,3 +193,33 @@ def test_fp8_every_v_code_widens_exactly(d):
     assert do <= 2e-2 * 7 / 6, do
     lg, lr = l.double().numpy(), rl
     assert np.all(np.abs(lg - lr) <= 1e-3 + FP8_LSE_REL * np.abs(lr))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_gqa_equals_expanded_mha_bitwise(causal, d):
+    """GQA equals MHA on repeat-interleaved K/V (glossary snippet), bit for
+    bit: each row's arithmetic is the same in both runs."""
+    w = gi.fixed_fp8(2, 8, 2, 300, 300, d, seed=52, causal=causal, q_scale=0.5, k_scale=0.25,
+                     v_scale=0.5)
+    o1, l1 = run_fp8(w)
+    rep = lambda t: t.view(torch.uint8).repeat_interleave(4, dim=2).contiguous().view(
+        torch.float8_e4m3fn)
+    wx = gi.Workload("mha_fp8", w.q, rep(w.k), rep(w.v), causal, w.scale, fp8_scales=w.fp8_scales)
+    o2, l2 = run_fp8(wx)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_fp8_varlen_equals_per_sequence_bitwise():
+    lens = [100, 1, 257, 64]
+    w = gi.varlen_fp8(lens, lens, 8, 2, 128, seed=53, causal=True, q_scale=0.5, k_scale=0.25,
+                      v_scale=0.5)
+    o, l = run_fp8(w)
+    cu = w.cu_seqlens_q.tolist()
+    for b in range(len(lens)):
+        sl = lambda t: t[None, cu[b]:cu[b + 1]].contiguous()
+        wb = gi.Workload("seq_fp8", sl(w.q), sl(w.k), sl(w.v), True, w.scale,
+                         fp8_scales=w.fp8_scales)
+        ob, lb = run_fp8(wb)
+        assert torch.equal(o[cu[b]:cu[b + 1]], ob[0])
+        assert torch.equal(l[cu[b]:cu[b + 1]], lb[0].T)
