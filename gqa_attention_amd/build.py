@@ -5,7 +5,9 @@ Usage: python -m gqa_attention_amd.build [-v]
 Every library source under csrc/ is compiled to an object in parallel, then linked
 into ``gqa_attention_amd/libgqa_attn.so``; ``csrc/hbm_probe.hip`` becomes the
 ``gqa_attention_amd/hbm_probe`` program (copy and read-stream reference
-kernels used to scale HBM byte counters). Packed-fp32 VALU instructions are
+kernels used to scale HBM byte counters) and ``csrc/issue_probe.hip`` the
+``gqa_attention_amd/issue_probe`` program (whether the matrix cores run while
+the same SIMD issues vector instructions). Packed-fp32 VALU instructions are
 disabled for device code (-packed-fp32-ops).
 """
 from __future__ import annotations
@@ -22,6 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgqa_attn.so")
 PROBE = os.path.join(PKG, "hbm_probe")  # copy / read-stream reference program
+PROBES = {"hbm_probe": "hbm_probe.hip", "issue_probe": "issue_probe.hip"}
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode_bf16.hip", "bwd_bf16.hip"]
@@ -70,11 +73,13 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
     os.replace(tmp, LIB)
-    cmd = [hipcc(), *COMMON, os.path.join(CSRC, "hbm_probe.hip"), "-o", PROBE + ".tmp"]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"hbm_probe build failed:\n{res.stderr}")
-    os.replace(PROBE + ".tmp", PROBE)
+    for prog, src in PROBES.items():
+        out = os.path.join(PKG, prog)
+        cmd = [hipcc(), *COMMON, os.path.join(CSRC, src), "-o", out + ".tmp"]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"{prog} build failed:\n{res.stderr}")
+        os.replace(out + ".tmp", out)
     return LIB
 
 
