@@ -1,17 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark of the fused GQA attention forward / split-KV decode on one MI355X.
 
-Default run (N = 1): the BERT-base encoder workload (B 64, S 512, 12 heads,
-d 64, non-causal, bf16) through ``gqa_attn_fwd``; one step = one forward over
-the batch with inputs already resident in HBM. Three input sets are rotated
-so consecutive launches never hit the same buffers (the set of one launch fits
-the 256 MB Infinity Cache; three do not).
+Default run (N = 1): the largest single-GPU workload, the packed
+variable-length causal GQA batch (48 query / 12 K/V heads, d 128, 32
+sequences of 128-4096 tokens, T = 77,493, bf16) through ``gqa_attn_fwd``; one
+step = one forward over the whole packed batch with inputs already resident
+in HBM (2.4 GB per launch, far above the 256 MB Infinity Cache).
 
 Printed: ONE JSON line with the metric, the dominant kernel's roofline
 (algorithmic flops or bytes per launch / launch time from HIP events on the
-launch stream), the CPU oracle timed on a bounded sample (rank 0, N = 1) and,
-under "extra", the other workloads (8192-token causal GQA prefill, split-KV
-decode at num_splits 1/2/4/8, packed variable-length causal GQA, tiny fp32,
+launch stream; median and minimum of single launches too), the CPU oracle
+timed on a bounded sample as a process pool (rank 0, N = 1) and, under
+"extra", the other workloads (8192-token causal GQA prefill, the BERT-base
+encoder, split-KV decode at num_splits 1/2/4/8, tiny fp32,
 the backward pass on the encoder, prefill and varlen workloads, and decode over
 general caches: ragged paged bf16 and fp8, sliding window; the fp8-input
 forward on the prefill and encoder shapes).
@@ -137,6 +138,20 @@ def run_timed(torch, step, steps, warmup, warm_seconds=0.0, timed_seconds=None):
     return wall, start.elapsed_time(end) / steps, steps
 
 
+def single_launches(torch, step, n, first=0):
+    """n back-to-back launches with an event between consecutive ones (after
+    the timed region): median and minimum single-launch time in ms."""
+    import statistics
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record()
+    for j in range(n):
+        step(first + j)
+        ev[j + 1].record()
+    torch.cuda.synchronize()
+    ts = [ev[j].elapsed_time(ev[j + 1]) for j in range(n)]
+    return statistics.median(ts), min(ts)
+
+
 def to_device(torch, w, sets):
     import gqa_inputs  # noqa: F401
     out = []
@@ -152,7 +167,7 @@ def to_device(torch, w, sets):
     return out
 
 
-def bench_fwd(torch, ga, w, steps, warmup, sets, **warm):
+def bench_fwd(torch, ga, w, steps, warmup, sets, singles=0, **warm):
     dev_sets = to_device(torch, w, sets)
     cq = w.cu_seqlens_q.cuda() if w.varlen else None
     ck = w.cu_seqlens_k.cuda() if w.varlen else None
@@ -180,6 +195,9 @@ def bench_fwd(torch, ga, w, steps, warmup, sets, **warm):
         plans[i % sets].run()
 
     wall, avg_ms, steps = run_timed(torch, step, steps, warmup, **warm)
+    med_ms = min_ms = None
+    if singles:
+        med_ms, min_ms = single_launches(torch, step, singles)
     if w.varlen:
         cu = w.cu_seqlens_q.tolist()
         flops = sum(fwd_flops(cu[b + 1] - cu[b], cu[b + 1] - cu[b], w.q.shape[1], w.q.shape[2],
@@ -187,7 +205,7 @@ def bench_fwd(torch, ga, w, steps, warmup, sets, **warm):
     else:
         B, S, H, d = w.q.shape
         flops = B * fwd_flops(S, w.k.shape[1], H, d, w.causal)
-    return dict(flops=flops, wall=wall, avg_ms=avg_ms, steps=steps)
+    return dict(flops=flops, wall=wall, avg_ms=avg_ms, steps=steps, med_ms=med_ms, min_ms=min_ms)
 
 
 def bench_decode(torch, ga, w, ns, steps, warmup, sets, **warm):
@@ -260,33 +278,48 @@ def bench_decode_ex(torch, ga, wc, ns, steps, warmup, **warm):
     return dict(bytes=cache_kv_bytes(wc), wall=wall, avg_ms=avg_ms, steps=steps)
 
 
-def cpu_baseline(w, budget_s=15.0):
-    """The fp64 oracle as it stands, on the first batches of the workload until
-    about `budget_s` seconds of CPU work; reported in the metric's unit."""
+def cpu_baseline(w, frac=0.25):
+    """The fp64 oracle as it stands, run as a process pool (one worker per
+    core this process may use, capped at 16, BLAS threads 1; oracle.pool) on
+    a bounded sample of the same workload: the leading sequences (varlen) or
+    batches (fixed length) that hold about `frac` of its work. Reported in the
+    metric's unit: algorithmic flops of the sample / wall time."""
     import numpy as np
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    B = w.q.shape[0]
-    done, flops = 0, 0
-    t0 = time.perf_counter()
-    while done < B and (time.perf_counter() - t0) < budget_s:
-        if w.fp8_scales is not None:
-            oracle.attention_fp8(w.q[done:done + 1], w.k[done:done + 1], w.v[done:done + 1],
-                                 w.scale, w.causal, *w.fp8_scales)
-        else:
-            oracle.attention(w.q[done:done + 1], w.k[done:done + 1], w.v[done:done + 1],
-                             w.scale, w.causal)
-        flops += fwd_flops(w.q.shape[1], w.k.shape[1], w.q.shape[2], w.q.shape[3], w.causal)
-        done += 1
-    el = time.perf_counter() - t0
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+    from oracle import pool as opool
+    if w.varlen:
+        cu = w.cu_seqlens_q.tolist()
+        ck = w.cu_seqlens_k.tolist()
+        work = [(cu[b + 1] - cu[b]) * (ck[b + 1] - ck[b]) for b in range(len(cu) - 1)]
+        n, acc = 0, 0
+        while n < len(work) and (acc < frac * sum(work) or n == 0):
+            acc += work[n]
+            n += 1
+        q, k, v = w.q[:cu[n]], w.k[:ck[n]], w.v[:ck[n]]
+        cq, ckk = cu[:n + 1], ck[:n + 1]
+        flops = sum(fwd_flops(cu[b + 1] - cu[b], ck[b + 1] - ck[b], w.q.shape[1], w.q.shape[2],
+                              w.causal) for b in range(n))
+        what = f"the first {n} of {len(cu) - 1} sequences ({cu[n]} of {cu[-1]} tokens)"
+    else:
+        B = w.q.shape[0]
+        n = max(1, int(round(frac * B)))
+        q, k, v = w.q[:n], w.k[:n], w.v[:n]
+        cq = ckk = None
+        flops = n * fwd_flops(w.q.shape[1], w.k.shape[1], w.q.shape[2], w.q.shape[3], w.causal)
+        what = f"the first {n} of {B} batch entries"
+    if w.fp8_scales is not None:
+        from oracle import fp8_forward as of8
+        q, k, v = of8.dequantised(q, k, v, *w.fp8_scales)
+    st = {}
+    opool.attention_pooled(q, k, v, w.scale, w.causal, cq, ckk, stats=st)
+    el = st["wall_s"]
+    return {"value": round(flops / el / 1e12, 5), "unit": "TFLOP/s", "cores": int(st["workers"]),
             "kind": "oracle",
-            "sample": f"{done} of {B} sequences (all {w.q.shape[2]} heads each), fp64 NumPy, "
-                      f"{el:.1f} s"}
+            "sample": f"{what}, all {w.q.shape[-2]} heads; fp64 NumPy oracle (S and P "
+                      f"materialised, so causal work is done in full) as {st['workers']} "
+                      f"processes x 1 BLAS thread, {st['units']} (sequence, head, row block) "
+                      f"units, {el:.1f} s wall",
+            "affinity_cores": opool.affinity_cores(), "cpu_model": opool.cpu_model(),
+            "wall_s": round(el, 2), "sample_gflop": round(flops / 1e9, 3)}
 
 
 def summarize_counters(pmc_dir: str, out_path: str) -> dict:
@@ -360,12 +393,16 @@ WORKLOAD_NAMES = {
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The defaults warm up for about 25 ms of encoder launches: MI355X clocks
-    # ramp over the first ~20 ms of back-to-back work (launches there run up
-    # to 25 % slower).
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--workload", default="bert_base_encoder",
+    # MI355X clocks ramp over the first ~20 ms of back-to-back work (launches
+    # there run up to 25 % slower): after the W warm-up steps the main line
+    # keeps warming up until --warm-ms of launches have run, then times
+    # exactly K steps.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warm-ms", type=float, default=100.0)
+    ap.add_argument("--singles", type=int, default=50,
+                    help="single launches timed one by one after the K steps (median, min)")
+    ap.add_argument("--workload", default="varlen_packed_causal",
                     choices=["bert_base_encoder", "llama31_8b_prefill", "llama31_8b_decode",
                              "varlen_packed_causal", "tiny_causal_gqa_fp32",
                              "decode_ragged_paged", "decode_ragged_paged_fp8",
@@ -413,12 +450,14 @@ def main():
         return "fwd_f32", "f32", PEAK_FP32_TFLOPS, "alu"
 
     def fwd_entry(name, w, steps, warmup, sets, **warm):
-        r = bench_fwd(torch, ga, w, steps, warmup, sets, **warm)
+        r = bench_fwd(torch, ga, w, steps, warmup, sets, singles=20, **warm)
         tf = r["flops"] / (r["avg_ms"] * 1e-3) / 1e12
         kernel, _, peak, _ = fwd_kind(w)
         return r, {"workload": w.name, "kernel": kernel, "tflops": round(tf, 2),
                    "peak": round(peak, 1), "frac_peak": round(tf / peak, 4),
                    "ms_per_launch": round(r["avg_ms"], 5),
+                   "ms_per_launch_median": round(r["med_ms"], 5),
+                   "ms_per_launch_min": round(r["min_ms"], 5),
                    "gflop": round(r["flops"] / 1e9, 3)}
 
     loaders = {
@@ -495,7 +534,8 @@ def main():
                   "Sk": w.k.shape[1], "d": w.q.shape[2], "num_splits": args.num_splits,
                   "kv_bytes": r["bytes"], "input_sets_rotated": sets}
     else:
-        r = bench_fwd(torch, ga, w, args.steps, args.warmup, sets)
+        r = bench_fwd(torch, ga, w, args.steps, args.warmup, sets, singles=args.singles,
+                      warm_seconds=args.warm_ms * 1e-3)
         tf = r["flops"] / (r["avg_ms"] * 1e-3) / 1e12
         value = r["flops"] * args.steps / r["wall"] / 1e12
         unit = "TFLOP/s"
@@ -516,6 +556,11 @@ def main():
     roof["traffic"] = traffic
     roof["kernel"] = kernel
     roof["launch_ms"] = round(r["avg_ms"], 5)
+    if r.get("med_ms"):
+        roof["launch_ms_median"] = round(r["med_ms"], 5)
+        roof["launch_ms_min"] = round(r["min_ms"], 5)
+        roof["single_launches"] = args.singles
+    roof["warmup_gpu_ms"] = args.warm_ms
 
     line = {"metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup,
@@ -569,6 +614,7 @@ def main():
 
     if not args.no_cpu_baseline and not w.decode:
         line["cpu_baseline"] = cpu_baseline(w)
+        line["cpu_baseline"]["gpu_speedup"] = round(roof["achieved"] / line["cpu_baseline"]["value"], 1)
     elif not args.no_cpu_baseline:
         import oracle
         t0 = time.perf_counter()

@@ -37,3 +37,13 @@ def test_source_digest_ignores_comments_not_code(tmp_path):
     c.write_text("int f(int x) {\n    return x + 2;\n}\n")
     assert bench.source_digest([str(a)]) == bench.source_digest([str(b)])
     assert bench.source_digest([str(a)]) != bench.source_digest([str(c)])
+
+
+def test_cpu_baseline_pool_on_a_small_varlen_batch():
+    import gqa_inputs
+    w = gqa_inputs.varlen([40, 10, 70, 30], [40, 10, 70, 30], 4, 1, 64, seed=3, causal=True)
+    cb = bench.cpu_baseline(w, frac=0.5)
+    assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["value"] > 0
+    assert 1 <= cb["cores"] <= cb["affinity_cores"] or cb["cores"] <= 16
+    assert "first 3 of 4 sequences" in cb["sample"]  # 40^2 + 10^2 < 50 % <= + 70^2
+    assert cb["cpu_model"]

@@ -10,7 +10,7 @@ matrix core's sums of 64 products are not carried in full fp32 (see
 FP8_LSE_REL). Shapes span several 32-key tiles
 and 128 / 256-row tiles with ragged tails, both head dims, MHA / GQA (G = 3,
 4) / MQA ratios, causal and not with Lq != Lk, fixed and variable length with
-empty sequences, and the two full-size fp8 workloads at sampled rows.
+empty sequences, and the two full-size fp8 workloads at every row.
 """
 import numpy as np
 import pytest
@@ -19,6 +19,7 @@ import torch
 import gqa_attention_amd as ga
 import gqa_inputs as gi
 from oracle import fp8_forward as of8
+from oracle import pool
 from parity_util import TOL
 
 pytestmark = pytest.mark.gpu
@@ -144,20 +145,14 @@ def test_fp8_deterministic():
 
 
 @pytest.mark.parametrize("name", ["llama31_8b_prefill_fp8", "bert_base_encoder_fp8"])
-def test_fp8_full_size_sampled(name):
-    """The full-size fp8 workloads: O and LSE at sampled rows (plus the first
-    and last row) against the sampled oracle."""
+def test_fp8_full_size_every_row(name):
+    """The full-size fp8 workloads, every row and head, against the oracle
+    on the dequantised inputs (run as a process pool)."""
     w = gi.NAMED[name]()
     o, l = run_fp8(w)
-    B, S, Hq, _ = w.q.shape
-    g = torch.Generator().manual_seed(49)
-    pick = lambda n, hi: torch.randint(0, hi, (n,), generator=g).tolist()
-    rows = list(zip(pick(40, B), pick(40, S), pick(40, Hq))) + [(0, 0, 0), (B - 1, S - 1, Hq - 1)]
-    qs, ks, vs = w.fp8_scales
-    ro, rl = of8.attention_rows_fp8(w.q, w.k, w.v, w.scale, w.causal, qs, ks, vs, rows)
-    got_o = torch.stack([o[b, i, h] for b, i, h in rows])
-    got_l = torch.tensor([float(l[b, h, i]) for b, i, h in rows])
-    compare(got_o, got_l, ro, rl, torch.bfloat16, f"fp8 full-size {name}")
+    qv, kv, vv = of8.dequantised(w.q, w.k, w.v, *w.fp8_scales)
+    ro, rl = pool.attention_pooled(qv, kv, vv, w.scale, w.causal)
+    print(name, compare(o, l, ro, rl, torch.bfloat16, f"fp8 full-size {name}"))
 
 
 @pytest.mark.parametrize("qs,ks", [(8.0, 8.0), (1.0 / 64, 1.0 / 64)])

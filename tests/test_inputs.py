@@ -1,18 +1,30 @@
-"""The seeded generators are deterministic and reproduce the glossary snippet's draws."""
+"""The seeded generators are deterministic; the tiny workload keeps the
+glossary example's draws (checked against stored checksums)."""
+import hashlib
+import json
+import os
+
 import torch
 
 import gqa_inputs
 
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "tiny_inputs.json")
 
-def test_tiny_matches_snippet_draws():
-    torch.manual_seed(0)
-    q = torch.randn(1, 8, 16, 64)
-    k = torch.randn(1, 2, 16, 64)
-    v = torch.randn(1, 2, 16, 64)
+
+def test_tiny_draws_match_stored_checksums():
+    """tests/golden/tiny_inputs.json (written by make_tiny_inputs.py next to
+    it) holds the SHA-256 of q, k, v in the head-major order they are drawn
+    in (glossary page "Grouped Query Attention (GQA)", section "How GQA
+    works": seed 0, q [1, 8, 16, 64] then k and v [1, 2, 16, 64]), and their
+    first values. The workload stores them token-major, causal, scale 1/8."""
+    ref = json.load(open(GOLDEN))
     w = gqa_inputs.tiny_causal_gqa_fp32()
-    assert torch.equal(w.q, q.transpose(1, 2))
-    assert torch.equal(w.k, k.transpose(1, 2))
-    assert torch.equal(w.v, v.transpose(1, 2))
+    for name, t in (("q", w.q), ("k", w.k), ("v", w.v)):
+        bhsd = t.transpose(1, 2).contiguous()
+        assert t.dtype == torch.float32
+        assert list(bhsd.shape) == ref[name]["shape_bhsd"]
+        assert hashlib.sha256(bhsd.numpy().tobytes()).hexdigest() == ref[name]["sha256_fp32"]
+        assert bhsd.flatten()[:4].tolist() == ref[name]["first4"]
     assert w.causal and abs(w.scale - 0.125) < 1e-12
 
 
