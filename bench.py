@@ -208,7 +208,7 @@ def bench_fwd(torch, ga, w, steps, warmup, sets, singles=0, **warm):
     return dict(flops=flops, wall=wall, avg_ms=avg_ms, steps=steps, med_ms=med_ms, min_ms=min_ms)
 
 
-def bench_decode(torch, ga, w, ns, steps, warmup, sets, **warm):
+def bench_decode(torch, ga, w, ns, steps, warmup, sets, singles=0, **warm):
     dev_sets = to_device(torch, w, sets)
     B, Hq, d = w.q.shape
     out = torch.empty_like(dev_sets[0][0])
@@ -224,8 +224,12 @@ def bench_decode(torch, ga, w, ns, steps, warmup, sets, **warm):
         plans[i % sets].run()
 
     wall, avg_ms, steps = run_timed(torch, step, steps, warmup, **warm)
+    med_ms = min_ms = None
+    if singles:
+        med_ms, min_ms = single_launches(torch, step, singles)
     kv_bytes = 2 * w.k.numel() * w.k.element_size()
-    return dict(bytes=kv_bytes, wall=wall, avg_ms=avg_ms, steps=steps)
+    return dict(bytes=kv_bytes, wall=wall, avg_ms=avg_ms, steps=steps, med_ms=med_ms,
+                min_ms=min_ms)
 
 
 def bench_bwd(torch, ga, w, steps, warmup, **warm):
@@ -501,7 +505,8 @@ def main():
 
     if args.workload in gqa_inputs.CACHE_NAMED:
         w = gqa_inputs.CACHE_NAMED[args.workload]()
-        r, e = cache_entry(w, args.num_splits, args.steps, args.warmup)
+        r, e = cache_entry(w, args.num_splits, args.steps, args.warmup,
+                           warm_seconds=args.warm_ms * 1e-3)
         gbs = e["kv_gbs"]
         line = {"metric": METRIC, "value": round(r["bytes"] * args.steps / r["wall"] / 1e9, 3),
                 "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -522,7 +527,8 @@ def main():
     w = loaders[args.workload]()
     sets = sets_for.get(args.workload, 1)
     if w.decode:
-        r = bench_decode(torch, ga, w, args.num_splits, args.steps, args.warmup, sets)
+        r = bench_decode(torch, ga, w, args.num_splits, args.steps, args.warmup, sets,
+                         singles=args.singles, warm_seconds=args.warm_ms * 1e-3)
         gbs = r["bytes"] / (r["avg_ms"] * 1e-3) / 1e9
         value = r["bytes"] * args.steps / r["wall"] / 1e9
         unit, dtype_s = "GB/s", "bf16"

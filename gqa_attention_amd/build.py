@@ -7,7 +7,10 @@ into ``gqa_attention_amd/libgqa_attn.so``; ``csrc/hbm_probe.hip`` becomes the
 ``gqa_attention_amd/hbm_probe`` program (copy and read-stream reference
 kernels used to scale HBM byte counters) and ``csrc/issue_probe.hip`` the
 ``gqa_attention_amd/issue_probe`` program (whether the matrix cores run while
-the same SIMD issues vector instructions). Packed-fp32 VALU instructions are
+the same SIMD issues vector instructions; ``issue_probe_vform`` is the same
+program with the matrix accumulators forced into ordinary VGPRs) and
+``csrc/mfma_fp8_probe.hip`` the ``gqa_attention_amd/mfma_fp8_probe`` program
+(how the fp8 matrix core sums its 64 products). Packed-fp32 VALU instructions are
 disabled for device code (-packed-fp32-ops).
 """
 from __future__ import annotations
@@ -24,7 +27,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgqa_attn.so")
 PROBE = os.path.join(PKG, "hbm_probe")  # copy / read-stream reference program
-PROBES = {"hbm_probe": "hbm_probe.hip", "issue_probe": "issue_probe.hip"}
+PROBES = {"hbm_probe": ("hbm_probe.hip", []), "issue_probe": ("issue_probe.hip", []),
+          "issue_probe_vform": ("issue_probe.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+          "mfma_fp8_probe": ("mfma_fp8_probe.hip", [])}
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode_bf16.hip", "bwd_bf16.hip"]
@@ -73,9 +78,9 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
     os.replace(tmp, LIB)
-    for prog, src in PROBES.items():
+    for prog, (src, extra) in PROBES.items():
         out = os.path.join(PKG, prog)
-        cmd = [hipcc(), *COMMON, os.path.join(CSRC, src), "-o", out + ".tmp"]
+        cmd = [hipcc(), *COMMON, *extra, os.path.join(CSRC, src), "-o", out + ".tmp"]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError(f"{prog} build failed:\n{res.stderr}")

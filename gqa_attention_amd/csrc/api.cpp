@@ -32,6 +32,17 @@ bool pack_enabled() {
 
 int status_from(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ELAUNCH; }
 
+// Pointers into a decode workspace (num_splits > 1; both null otherwise).
+void split_workspace(void *workspace, int B, int Hq, int d, int num_splits, float *&ws_o,
+                     float *&ws_lse) {
+    ws_o = nullptr;
+    ws_lse = nullptr;
+    if (num_splits <= 1) return;
+    ws_o = static_cast<float *>(workspace);
+    ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                       gqa::decode_workspace_o_bytes(B, Hq, d, num_splits));
+}
+
 }  // namespace
 
 extern "C" {
@@ -197,12 +208,7 @@ int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache, voi
     const int chunk = gqa::split_chunk(Sk, num_splits);
     const int rows = B * Hq;
     float *ws_o = nullptr, *ws_lse = nullptr;
-    if (num_splits > 1) {
-        size_t o_bytes = (size_t)num_splits * rows * d * sizeof(float);
-        o_bytes = (o_bytes + 255) & ~size_t(255);
-        ws_o = static_cast<float *>(workspace);
-        ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
-    }
+    split_workspace(workspace, B, Hq, d, num_splits, ws_o, ws_lse);
     (void)hipGetLastError();
     if (dtype == GQA_DTYPE_BF16) {
         gqa::DecodeParams p{};
@@ -271,14 +277,8 @@ int gqa_attn_decode_ex(const void *q, const void *k_cache, const void *v_cache, 
                                            v_scale, num_splits, workspace, workspace_bytes);
     if (rc != GQA_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int rows = B * Hq;
     float *ws_o = nullptr, *ws_lse = nullptr;
-    if (num_splits > 1) {
-        size_t o_bytes = (size_t)num_splits * rows * d * sizeof(float);
-        o_bytes = (o_bytes + 255) & ~size_t(255);
-        ws_o = static_cast<float *>(workspace);
-        ws_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) + o_bytes);
-    }
+    split_workspace(workspace, B, Hq, d, num_splits, ws_o, ws_lse);
     const bool fp8 = kv_dtype == GQA_DTYPE_FP8_E4M3;
     gqa::DecodeParams p{};
     p.q = q;
@@ -307,8 +307,8 @@ int gqa_attn_decode_ex(const void *q, const void *k_cache, const void *v_cache, 
     (void)hipGetLastError();
     hipError_t e = gqa::launch_decode_bf16(p, d, block_table != nullptr, fp8, s);
     if (e != hipSuccess || num_splits == 1) return status_from(e);
-    return status_from(
-        gqa::launch_decode_combine(ws_o, ws_lse, out, lse, rows, num_splits, d, true, s));
+    return status_from(gqa::launch_decode_combine(ws_o, ws_lse, out, lse, B * Hq, num_splits, d,
+                                                  true, s));
 }
 
 }  // extern "C"

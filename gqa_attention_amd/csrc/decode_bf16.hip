@@ -382,6 +382,13 @@ decode_bf16_kernel(DecodeParams p) {
 }
 
 // Merge num_splits partials per (batch, head) row: one wavefront per row.
+// Lane s reads L_s (num_splits <= 64), so the max M and the weights
+// w_s = exp(L_s - M) (0 for an empty split) come from one load per lane and
+// fixed-order shuffle trees; then the lanes sum w_s O_s over s in split
+// order with the row's O_s loads unrolled and independent, so the merge pays
+// about one memory latency rather than one per split. An empty split's O_s
+// is never written: it is read (inside the workspace) but multiplied by
+// nothing (selected to 0).
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ ws_o,
                                                       const float *__restrict__ ws_lse,
@@ -390,21 +397,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, ws_lse[(int64_t)s * rows + row]);
+    const float ls = lane < ns ? ws_lse[(int64_t)lane * rows + row] : -INFINITY;
+    float M = ls;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float w = (ls == -INFINITY) ? 0.f : __expf(ls - M);
+    float tot = w;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    float tot = 0.f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < ns; ++s) {
-            const float ls = ws_lse[(int64_t)s * rows + row];
-            if (ls == -INFINITY) continue;  // empty split: its O_s is not written
-            const float w = __expf(ls - M);
-            tot += w;
-            const float *src = ws_o + ((int64_t)s * rows + row) * D;
+    const float *src = ws_o + (int64_t)row * D + lane;
+    const int64_t split_stride = (int64_t)rows * D;
+#pragma unroll 8
+    for (int s = 0; s < ns; ++s) {
+        const float ws = __shfl(w, s);
 #pragma unroll
-            for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, src[lane + 64 * e], acc[e]);
+        for (int e = 0; e < PER; ++e) {
+            const float v = src[s * split_stride + 64 * e];
+            acc[e] = fmaf(ws, ws != 0.f ? v : 0.f, acc[e]);
         }
     }
     const bool empty = !(tot > 0.f);

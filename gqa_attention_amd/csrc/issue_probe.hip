@@ -11,21 +11,37 @@
 //   E   32 v_exp_f32 on 16 independent chains (x <- 2^-|x|)
 //   MV  M and V in one wave, interleaved 1 MFMA : 8 FMA
 //   ME  M and E in one wave, interleaved 1 MFMA : 4 exp
+//   Mc  8 v_mfma_f32_32x32x16_bf16 accumulating into one accumulator
+//   Lb  8 ds_read_b128 (8 KiB per wave, the forward's K operand pattern)
+//   Lt  16 ds_read_b64_tr_b16 (8 KiB per wave, the forward's V^T pattern)
+//   Lbt both; X both plus the forward's softmax vector work for one tile
+//       (16 FMA, 16 exp, 16 add, 8 bf16 packs); L and X roles wait for
+//       their LDS reads at the end of each iteration
 // With 8 waves, waves w and w + 4 share a SIMD (checked from HW_ID); the first
 // role is run by waves 0-3, the second by waves 4-7. Cycles come from
 // s_memtime (shader clock) around the loop; the clock from the ratio to
 // s_memrealtime (100 MHz). All memory accesses are one store per wave slot of
 // the output array, indexed by workgroup and wave.
+//
+// The compiler keeps MFMA accumulators in AGPRs or in ordinary VGPRs by its
+// own heuristic (here: AGPRs, since a wave may use more than 256 registers);
+// the program issue_probe_vform is the same source built with
+// -mllvm -amdgpu-mfma-vgpr-form, which forces them into VGPRs as in the
+// attention kernels (two waves per SIMD, at most 256 registers).
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
 #include <cstdlib>
+#include <cstdint>
 #include <cstring>
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 
-enum Role { R_M = 1, R_V = 2, R_E = 3, R_MV = 4, R_ME = 5 };
+enum Role { R_M = 1, R_V = 2, R_E = 3, R_MV = 4, R_ME = 5, R_MC = 6, R_LB = 7, R_LT = 8, R_LBT = 9, R_X = 10 };
+
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 struct WaveRec {
     unsigned long long cycles, rtc;
@@ -37,6 +53,86 @@ __device__ __forceinline__ void loop_m(int iters, f32x16 (&acc)[4], bf16x8 a, bf
     for (int i = 0; i < iters; ++i) {
 #pragma unroll
         for (int g = 0; g < 8; ++g) acc[g & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[g & 3], 0, 0, 0);
+    }
+}
+
+// 8 MFMAs accumulating into one accumulator (a dependent chain)
+__device__ __forceinline__ void loop_mc(int iters, f32x16 (&acc)[4], bf16x8 a, bf16x8 b) {
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int g = 0; g < 8; ++g) acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[0], 0, 0, 0);
+    }
+}
+
+// LDS reads in the forward kernel's d = 128 operand patterns, 8 KiB per
+// wave each: 8 ds_read_b128 (a 32 x 128 bf16 K tile) and 16
+// ds_read_b64_tr_b16 (the transposed V tile). The values are kept alive by
+// empty asm statements; each iteration waits for its reads.
+struct LdsAddr {
+    uint32_t kb[8];  // byte offsets of the b128 reads
+    uint32_t vt[4];  // byte offsets of the transposing reads (+ 2048 / 4096 / 6144 for the others)
+};
+__device__ __forceinline__ LdsAddr lds_addr_of(int lane) {
+    LdsAddr a;
+    const int col = lane & 31, half = lane >> 5;
+    for (int s = 0; s < 8; ++s) a.kb[s] = (col * 128 + (((2 * s + half) ^ (col & 15)) * 8)) * 2;
+    const int vj = lane & 15, vg = lane >> 4;
+    const int v_row = 4 * (vg >> 1) + (vj >> 2);
+    for (int i = 0; i < 4; ++i) {
+        const int chunk = 4 * i + 2 * (vg & 1) + ((vj & 3) >> 1);
+        a.vt[i] = 16384 + (v_row * 128 + ((chunk ^ (4 * (v_row & 3))) * 8) + 4 * (vj & 1)) * 2;
+    }
+    return a;
+}
+__device__ __forceinline__ void lds_reads(const unsigned char *lds, const LdsAddr &a, bool b128, bool tr) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    if (b128) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const u32x4 v = *(const u32x4 *)(lds + a.kb[s]);
+            asm volatile("" ::"v"(v));
+        }
+    }
+    if (tr) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)(lds + a.vt[i] + 2048 * h));
+                asm volatile("" ::"v"(v));
+            }
+    }
+}
+__device__ __forceinline__ void loop_l(int iters, const unsigned char *lds, const LdsAddr &a, bool b128, bool tr) {
+    for (int i = 0; i < iters; ++i) {
+        lds_reads(lds, a, b128, tr);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+}
+// The forward step's softmax cluster: 16 x (FMA, exp, add), 8 bf16 packs,
+// with both LDS read patterns.
+__device__ __forceinline__ void loop_x(int iters, const unsigned char *lds, const LdsAddr &a, float (&x)[16],
+                                       float fa, float fb) {
+    for (int i = 0; i < iters; ++i) {
+        lds_reads(lds, a, true, true);
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+        uint32_t pk[8];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(x[j], fa, -fb));
+            part[j & 3] += p;
+            x[j] = p;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+            const bf2 v = {(__bf16)x[2 * j], (__bf16)x[2 * j + 1]};
+            pk[j] = __builtin_bit_cast(uint32_t, v);
+            asm volatile("" ::"v"(pk[j]));
+        }
+        x[0] += (part[0] + part[1]) + (part[2] + part[3]);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
 }
 
@@ -90,9 +186,11 @@ __device__ __forceinline__ void loop_me(int iters, f32x16 (&acc)[4], bf16x8 a, b
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void probe_kernel(WaveRec *out, int iters, int role_lo, int role_hi,
                                                         float fa, float fb) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_dyn[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int role = wave < 4 ? role_lo : role_hi;
+    const LdsAddr la = lds_addr_of(lane);
     f32x16 acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
@@ -114,6 +212,11 @@ __global__ __launch_bounds__(64 * NW) void probe_kernel(WaveRec *out, int iters,
     else if (role == R_E) loop_e(iters, x);
     else if (role == R_MV) loop_mv(iters, acc, a, b, x, fa, fb);
     else if (role == R_ME) loop_me(iters, acc, a, b, x);
+    else if (role == R_MC) loop_mc(iters, acc, a, b);
+    else if (role == R_LB) loop_l(iters, lds_dyn, la, true, false);
+    else if (role == R_LT) loop_l(iters, lds_dyn, la, false, true);
+    else if (role == R_LBT) loop_l(iters, lds_dyn, la, true, true);
+    else if (role == R_X) loop_x(iters, lds_dyn, la, x, fa, fb);
     const unsigned long long c1 = __builtin_amdgcn_s_memtime();
     const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
 
@@ -141,6 +244,11 @@ static const char *role_name(int r) {
     case R_E: return "E";
     case R_MV: return "MV";
     case R_ME: return "ME";
+    case R_MC: return "Mc";
+    case R_LB: return "Lb";
+    case R_LT: return "Lt";
+    case R_LBT: return "Lbt";
+    case R_X: return "X";
     default: return "-";
     }
 }
@@ -158,7 +266,9 @@ int main(int argc, char **argv) {
     const Case cases[] = {
         {4, R_M, R_M},   {4, R_V, R_V},   {4, R_E, R_E},   {4, R_MV, R_MV}, {4, R_ME, R_ME},
         {8, R_M, R_M},   {8, R_V, R_V},   {8, R_E, R_E},   {8, R_M, R_V},   {8, R_M, R_E},
-        {8, R_MV, R_MV}, {8, R_ME, R_ME},
+        {8, R_MV, R_MV}, {8, R_ME, R_ME}, {4, R_MC, R_MC}, {8, R_MC, R_V}, {8, R_MC, R_E},
+        {4, R_LB, R_LB}, {4, R_LT, R_LT}, {4, R_LBT, R_LBT}, {8, R_LBT, R_LBT}, {8, R_M, R_LBT},
+        {4, R_X, R_X},   {8, R_M, R_X},   {8, R_X, R_X},
     };
     const size_t lds = 96 * 1024;  // one workgroup per CU
     if (hipFuncSetAttribute((const void *)probe_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=

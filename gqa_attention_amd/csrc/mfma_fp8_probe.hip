@@ -1,0 +1,244 @@
+// fp8 matrix-core sum probe: how v_mfma_scale_f32_32x32x64_f8f6f4 (both
+// operands e4m3, unit scales) adds up its 64 products. Built as a small
+// program:
+//   mfma_fp8_probe [--dump] -> per test block, a table of the matrix core's
+//                      error against the exact sum of the products and C0
+//                      (computed on the host in double); --dump also prints
+//                      each block's codes, C0 and raw results
+//
+// One wavefront computes C = A B + C0 for a 32 x 64 A and a 64 x 32 B given
+// as e4m3 byte codes, with the operand layout the forward kernel uses: lane l
+// holds row (l mod 32) of A and column (l mod 32) of B, bytes
+// k = 32 (l / 32) .. + 31 of that row / column; output register r of lane l
+// is element (8 (r / 4) + 4 (l / 32) + r mod 4, l mod 32). Every device
+// access is within the three arrays copied in and the one copied out.
+//
+// Blocks:
+//  gap     C[i][j] = L_i * 448 + 63 * 2^-(j mod 10): one large product (row i:
+//          L_i = 448 / 2^(i / 2), rounded to e4m3) and 63 equal small ones,
+//          so the exponent gap between them runs over 1..27 bits
+//  c0      C0 = 2^20 + i, products as in gap with L = 0: the C input's add
+//  cancel  +L * 448 and -L * 448 and 62 small ones: the large pair cancels
+//  pos     one product 448 (row i: at k = pos[i]) among 63 of 2^-9: which
+//          small products share its fate
+//  neg     as gap with the 63 small products negative
+//  frac    as gap with small products 1.5 x 2^-(j mod 10)
+//  random  A, B random e4m3 codes of N(0, 1) values, C0 = 0: the error of
+//          ordinary sums
+//  c0rand  as random, with C0 of random magnitudes and random low bits
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <random>
+#include <vector>
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+__global__ __launch_bounds__(64) void mfma_kernel(const uint8_t *a, const uint8_t *b, const float *c0,
+                                                  float *out) {
+    const int l = threadIdx.x;
+    const int col = l & 31, half = l >> 5;
+    i32x8 av, bv;
+    for (int w = 0; w < 8; ++w) {
+        uint32_t x = 0, y = 0;
+        for (int e = 0; e < 4; ++e) {
+            const int k = 32 * half + 4 * w + e;
+            x |= (uint32_t)a[col * 64 + k] << (8 * e);  // A[col][k]
+            y |= (uint32_t)b[k * 32 + col] << (8 * e);  // B[k][col]
+        }
+        av[w] = (int)x;
+        bv[w] = (int)y;
+    }
+    f32x16 acc;
+    for (int r = 0; r < 16; ++r) acc[r] = c0[(8 * (r / 4) + 4 * half + (r & 3)) * 32 + col];
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
+    for (int r = 0; r < 16; ++r) out[(8 * (r / 4) + 4 * half + (r & 3)) * 32 + col] = acc[r];
+}
+
+// Value of an OCP e4m3 code (bias 7, subnormals, S.1111.111 = NaN).
+static double e4m3(uint8_t c) {
+    const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double v = e == 0 ? m / 8.0 * std::ldexp(1.0, -6) : (1 + m / 8.0) * std::ldexp(1.0, e - 7);
+    return s ? -v : v;
+}
+// Code of the e4m3 value nearest to v (ties to even code).
+static uint8_t nearest(double v) {
+    int best = 0;
+    double bd = INFINITY;
+    for (int c = 0; c < 256; ++c) {
+        const double x = e4m3((uint8_t)c);
+        if (std::isnan(x)) continue;
+        const double dd = std::fabs(x - v);
+        if (dd < bd || (dd == bd && (c & 1) == 0)) {
+            bd = dd;
+            best = c;
+        }
+    }
+    return (uint8_t)best;
+}
+
+struct Block {
+    const char *name;
+    std::vector<uint8_t> A, B;
+    std::vector<float> C0;
+    Block(const char *n) : name(n), A(32 * 64, 0), B(64 * 32, 0), C0(32 * 32, 0.f) {}
+};
+
+int main(int argc, char **argv) {
+    const bool dump = argc > 1 && strcmp(argv[1], "--dump") == 0;
+    std::vector<Block> blocks;
+    const uint8_t one = nearest(1.0), big = nearest(448.0);
+    {
+        Block bl("gap");
+        for (int i = 0; i < 32; ++i) {
+            bl.A[i * 64] = nearest(448.0 / std::ldexp(1.0, i / 2));
+            for (int k = 1; k < 64; ++k) bl.A[i * 64 + k] = one;
+        }
+        for (int j = 0; j < 32; ++j) {
+            bl.B[j] = big;
+            for (int k = 1; k < 64; ++k) bl.B[k * 32 + j] = nearest(std::ldexp(1.0, -(j % 10)));
+        }
+        blocks.push_back(bl);
+    }
+    {
+        Block bl("c0");
+        for (int i = 0; i < 32; ++i)
+            for (int k = 1; k < 64; ++k) bl.A[i * 64 + k] = one;
+        for (int j = 0; j < 32; ++j)
+            for (int k = 1; k < 64; ++k) bl.B[k * 32 + j] = nearest(std::ldexp(1.0, -(j % 10)));
+        for (int i = 0; i < 32; ++i)
+            for (int j = 0; j < 32; ++j) bl.C0[i * 32 + j] = (float)(std::ldexp(1.0, 20) + i);
+        blocks.push_back(bl);
+    }
+    {
+        Block bl("cancel");
+        for (int i = 0; i < 32; ++i) {
+            const uint8_t L = nearest(448.0 / std::ldexp(1.0, i / 2));
+            bl.A[i * 64] = L;
+            bl.A[i * 64 + 1] = L | 0x80;  // -L
+            for (int k = 2; k < 64; ++k) bl.A[i * 64 + k] = one;
+        }
+        for (int j = 0; j < 32; ++j) {
+            bl.B[j] = big;
+            bl.B[32 + j] = big;
+            for (int k = 2; k < 64; ++k) bl.B[k * 32 + j] = nearest(std::ldexp(1.0, -(j % 10)));
+        }
+        blocks.push_back(bl);
+    }
+    {
+        // row i: one 448 at k = pos[i], all other entries of A 2^-9, B all
+        // ones: which of the small products are dropped with the large one
+        Block bl("pos");
+        const int pos[32] = {0, 1, 3, 7, 8, 9, 15, 16, 17, 23, 24, 25, 31, 32, 33, 39,
+                             40, 41, 47, 48, 49, 55, 56, 57, 62, 63, 4, 12, 20, 28, 36, 60};
+        for (int i = 0; i < 32; ++i)
+            for (int k = 0; k < 64; ++k) bl.A[i * 64 + k] = k == pos[i] ? big : nearest(std::ldexp(1.0, -9));
+        for (int k = 0; k < 64; ++k)
+            for (int j = 0; j < 32; ++j) bl.B[k * 32 + j] = one;
+        blocks.push_back(bl);
+    }
+    {
+        // as gap, with the 63 small products negative
+        Block bl("neg");
+        for (int i = 0; i < 32; ++i) {
+            bl.A[i * 64] = nearest(448.0 / std::ldexp(1.0, i / 2));
+            for (int k = 1; k < 64; ++k) bl.A[i * 64 + k] = one | 0x80;
+        }
+        for (int j = 0; j < 32; ++j) {
+            bl.B[j] = big;
+            for (int k = 1; k < 64; ++k) bl.B[k * 32 + j] = nearest(std::ldexp(1.0, -(j % 10)));
+        }
+        blocks.push_back(bl);
+    }
+    {
+        // small products 1.5 x 2^-e (two bits): partial truncation of each
+        Block bl("frac");
+        for (int i = 0; i < 32; ++i) {
+            bl.A[i * 64] = nearest(448.0 / std::ldexp(1.0, i / 2));
+            for (int k = 1; k < 64; ++k) bl.A[i * 64 + k] = nearest(1.5);
+        }
+        for (int j = 0; j < 32; ++j) {
+            bl.B[j] = big;
+            for (int k = 1; k < 64; ++k) bl.B[k * 32 + j] = nearest(std::ldexp(1.0, -(j % 10)));
+        }
+        blocks.push_back(bl);
+    }
+    {
+        Block bl("random");
+        std::mt19937 g(12345);
+        std::normal_distribution<double> nd(0.0, 1.0);
+        for (auto &x : bl.A) x = nearest(2.0 * nd(g));
+        for (auto &x : bl.B) x = nearest(4.0 * nd(g));
+        blocks.push_back(bl);
+    }
+
+    {
+        // random products with C0 of random magnitude (2^-12 .. 2^12 times a
+        // normal value, all 24 bits set at random): how C enters the sum
+        Block bl("c0rand");
+        std::mt19937 g(777);
+        std::normal_distribution<double> nd(0.0, 1.0);
+        std::uniform_int_distribution<int> ue(-12, 12);
+        for (auto &x : bl.A) x = nearest(2.0 * nd(g));
+        for (auto &x : bl.B) x = nearest(4.0 * nd(g));
+        for (auto &x : bl.C0) x = (float)(nd(g) * std::ldexp(1.0, ue(g)));
+        blocks.push_back(bl);
+    }
+    uint8_t *da, *db;
+    float *dc, *dout;
+    if (hipMalloc(&da, 32 * 64) != hipSuccess || hipMalloc(&db, 64 * 32) != hipSuccess ||
+        hipMalloc(&dc, 32 * 32 * 4) != hipSuccess || hipMalloc(&dout, 32 * 32 * 4) != hipSuccess) {
+        printf("alloc failed\n");
+        return 1;
+    }
+    for (const Block &bl : blocks) {
+        float out[32 * 32];
+        if (hipMemcpy(da, bl.A.data(), 32 * 64, hipMemcpyHostToDevice) != hipSuccess ||
+            hipMemcpy(db, bl.B.data(), 64 * 32, hipMemcpyHostToDevice) != hipSuccess ||
+            hipMemcpy(dc, bl.C0.data(), 32 * 32 * 4, hipMemcpyHostToDevice) != hipSuccess)
+            return 1;
+        hipLaunchKernelGGL(mfma_kernel, dim3(1), dim3(64), 0, 0, da, db, dc, dout);
+        if (hipMemcpy(out, dout, sizeof(out), hipMemcpyDeviceToHost) != hipSuccess) return 1;
+        printf("== block %s: rows i, columns j; each entry (got - exact) in units of 2^-23 of the "
+               "largest |term| (product or C0) of that sum\n", bl.name);
+        double worst_rel = 0.0;
+        for (int i = 0; i < 32; ++i) {
+            printf("%2d:", i);
+            for (int j = 0; j < 32; ++j) {
+                double exact = bl.C0[i * 32 + j], mx = std::fabs(bl.C0[i * 32 + j]);
+                for (int k = 0; k < 64; ++k) {
+                    const double t = e4m3(bl.A[i * 64 + k]) * e4m3(bl.B[k * 32 + j]);
+                    exact += t;
+                    mx = std::fmax(mx, std::fabs(t));
+                }
+                const double err = (double)out[i * 32 + j] - exact;
+                const double units = mx > 0 ? err / (mx * std::ldexp(1.0, -23)) : 0.0;
+                if (exact != 0) worst_rel = std::fmax(worst_rel, std::fabs(err / exact));
+                if (j < 12) printf(" %9.3f", units);
+            }
+            printf("\n");
+        }
+        printf("   worst |got - exact| / |exact| in block %s: %.3e\n", bl.name, worst_rel);
+        if (dump) {  // the block's codes, C0 and results, for a model of the sums
+            printf("dump %s A", bl.name);
+            for (uint8_t x : bl.A) printf(" %02x", x);
+            printf("\ndump %s B", bl.name);
+            for (uint8_t x : bl.B) printf(" %02x", x);
+            printf("\ndump %s C0", bl.name);
+            for (float x : bl.C0) printf(" %a", x);
+            printf("\ndump %s OUT", bl.name);
+            for (float x : out) printf(" %a", x);
+            printf("\n");
+        }
+    }
+    if (hipFree(da) != hipSuccess || hipFree(db) != hipSuccess || hipFree(dc) != hipSuccess ||
+        hipFree(dout) != hipSuccess)
+        return 1;
+    return 0;
+}

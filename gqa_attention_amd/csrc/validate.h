@@ -53,13 +53,15 @@ inline int validate_fwd(const void *q, const void *k, const void *v, const void 
     return GQA_OK;
 }
 
+// Decode workspace (num_splits > 1): fp32 partial outputs [ns, B*Hq, d]
+// (the size rounded up to 256 bytes), then fp32 partial LSEs [ns, B*Hq].
+inline size_t decode_workspace_o_bytes(int B, int Hq, int d, int num_splits) {
+    return ((size_t)B * Hq * num_splits * d * sizeof(float) + 255) & ~size_t(255);
+}
 inline size_t decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
     if (B < 1 || Hq < 1 || !supported_d(d) || num_splits < 1 || num_splits > kMaxSplits) return 0;
     if (num_splits == 1) return 0;
-    const size_t rows = (size_t)B * Hq * num_splits;
-    size_t o_bytes = rows * d * sizeof(float);
-    o_bytes = (o_bytes + 255) & ~size_t(255);
-    return o_bytes + rows * sizeof(float);
+    return decode_workspace_o_bytes(B, Hq, d, num_splits) + (size_t)B * Hq * num_splits * sizeof(float);
 }
 
 inline int split_chunk(int Sk, int num_splits) {

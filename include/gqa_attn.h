@@ -162,10 +162,12 @@ int gqa_attn_bwd(const void *q, const void *k, const void *v, const void *out, c
 
 /*
  * gqa_attn_decode_workspace_bytes - size of the caller-owned workspace that
- * gqa_attn_decode needs for num_splits partial results (fp32 normalised
- * partial outputs [num_splits, B*Hq, d] followed by fp32 partial LSEs
- * [num_splits, B*Hq]). Returns 0 when num_splits == 1 (no workspace needed)
- * and 0 for invalid sizes (num_splits < 1, B, Hq < 1, d not in {64, 128}).
+ * gqa_attn_decode / gqa_attn_decode_ex need for num_splits partial results
+ * (fp32 normalised partial outputs [num_splits, B*Hq, d], the size rounded up
+ * to 256 bytes, followed by fp32 partial LSEs [num_splits, B*Hq]); the
+ * contents need no initialisation and are overwritten by every call.
+ * Returns 0 when num_splits == 1 (no workspace needed) and 0 for invalid
+ * sizes (num_splits < 1, B, Hq < 1, d not in {64, 128}).
  */
 size_t gqa_attn_decode_workspace_bytes(int B, int Hq, int d, int num_splits);
 

@@ -153,6 +153,21 @@ def test_decode_partials_match_oracle_per_split(dtype):
                 f"split {s}")
 
 
+def test_decode_workspace_is_reusable_across_shapes():
+    """One workspace, left as each call leaves it, serves later calls of
+    other shapes and split counts."""
+    ws = torch.empty(ga.decode_workspace_bytes(32, 32, 128, 8), dtype=torch.uint8, device="cuda")
+    cases = [(32, 32, 8, 700, 128, 8), (5, 8, 2, 333, 64, 4), (32, 32, 8, 700, 128, 2),
+             (3, 48, 12, 64, 128, 8), (32, 32, 8, 700, 128, 8)]
+    for i, (B, hq, hkv, sk, d, ns) in enumerate(cases):
+        w = gqa_inputs.decode(B, hq, hkv, sk, d, seed=78 + i)
+        o, l = ga.decode(w.q.cuda(), w.k.cuda(), w.v.cuda(), scale=w.scale, num_splits=ns,
+                         workspace=ws)
+        torch.cuda.synchronize()
+        ro, rl = oracle.decode(w.q, w.k, w.v, w.scale)
+        compare(o.cpu(), l.cpu(), ro, rl, torch.bfloat16, f"decode reuse {i}")
+
+
 # ---------------------------------------------------------------------------
 # Invariants that hold bit for bit on the GPU.
 # ---------------------------------------------------------------------------
