@@ -26,6 +26,8 @@
 //  random  A, B random e4m3 codes of N(0, 1) values, C0 = 0: the error of
 //          ordinary sums
 //  c0rand  as random, with C0 of random magnitudes and random low bits
+//  c0one   C0 as c0rand plus a single product per sum
+//  c0two   C0 as c0rand plus two products per sum, 32 k apart
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -186,6 +188,34 @@ int main(int argc, char **argv) {
         std::normal_distribution<double> nd(0.0, 1.0);
         std::uniform_int_distribution<int> ue(-12, 12);
         for (auto &x : bl.A) x = nearest(2.0 * nd(g));
+        for (auto &x : bl.B) x = nearest(4.0 * nd(g));
+        for (auto &x : bl.C0) x = (float)(nd(g) * std::ldexp(1.0, ue(g)));
+        blocks.push_back(bl);
+    }
+    {
+        // one product per sum: A row i is nonzero only at k = i, B only in
+        // k < 32, so C[i][j] = C0 + A[i][i] B[i][j] (k = i lies in group i / 8)
+        Block bl("c0one");
+        std::mt19937 g(4242);
+        std::normal_distribution<double> nd(0.0, 1.0);
+        std::uniform_int_distribution<int> ue(-12, 12);
+        for (int i = 0; i < 32; ++i) bl.A[i * 64 + i] = nearest(2.0 * nd(g));
+        for (int k = 0; k < 32; ++k)
+            for (int j = 0; j < 32; ++j) bl.B[k * 32 + j] = nearest(4.0 * nd(g));
+        for (auto &x : bl.C0) x = (float)(nd(g) * std::ldexp(1.0, ue(g)));
+        blocks.push_back(bl);
+    }
+    {
+        // two products per sum, at k = i and k = i + 32 (groups i / 8 and
+        // 4 + i / 8)
+        Block bl("c0two");
+        std::mt19937 g(4343);
+        std::normal_distribution<double> nd(0.0, 1.0);
+        std::uniform_int_distribution<int> ue(-12, 12);
+        for (int i = 0; i < 32; ++i) {
+            bl.A[i * 64 + i] = nearest(2.0 * nd(g));
+            bl.A[i * 64 + i + 32] = nearest(2.0 * nd(g));
+        }
         for (auto &x : bl.B) x = nearest(4.0 * nd(g));
         for (auto &x : bl.C0) x = (float)(nd(g) * std::ldexp(1.0, ue(g)));
         blocks.push_back(bl);
