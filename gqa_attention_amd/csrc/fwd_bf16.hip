@@ -43,8 +43,15 @@
 //  * Workgroup order: the row tiles of a head group run back to back on one
 //    XCD (workgroups are dealt round-robin to the 8 XCDs), so its K/V comes
 //    from HBM once and is then reused from that XCD's L2; causal row tiles are
-//    issued heaviest first.
+//    issued heaviest first. For variable-length batches the workgroups are
+//    persistent: as many as the device holds at once, each claiming row
+//    tiles from per-XCD lists until none is left (see "Workgroup scheduling"
+//    below).
 
+#include <algorithm>
+#include <atomic>
+#include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "device_util.h"
@@ -62,6 +69,9 @@ namespace {
 #endif
 #ifndef GQA_VR_DIV
 #define GQA_VR_DIV 1
+#endif
+#ifndef GQA_PINGPONG
+#define GQA_PINGPONG 1
 #endif
 
 // Wavefronts per workgroup (32 query rows each): 8 at d = 128, where sharing
@@ -113,9 +123,22 @@ struct Cfg {
 // exactly to bf16 into one of two bf16 V slots, so P stays bf16 and O^T += V^T
 // P^T runs as in the bf16 kernel: the result is the attention of the
 // dequantised inputs, rounded as in the bf16 path.
+template <int D, bool F8>
+struct Ring {
+    static constexpr bool PP = D == 128 && !F8 && GQA_PINGPONG;
+    static constexpr int SLOT = Cfg<D>::BN * D;      // elements per slot
+    static constexpr int NKS = PP ? 5 : 4;             // K slots
+    static constexpr int NVS = F8 ? 2 : (PP ? 5 : 4);  // V slots (F8: bf16 V)
+    static constexpr int ELEMS = (NKS + NVS) * SLOT + Waves<D>::BM * D;
+};
+
+// One row tile: rows rb * BM .. of head group hg (sequence b), with the
+// workgroup's LDS (Ring<D, F8>::ELEMS bf16). Every thread of the workgroup
+// calls it; it issues no barrier before its first DMA, so the caller must
+// order it after any earlier use of the LDS.
 template <int D, bool CAUSAL, bool VARLEN, bool F8>
-__global__ __launch_bounds__(Waves<D>::NTHREADS) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2))) void
-fwd_bf16_kernel(FwdParams p) {
+__device__ __forceinline__ void fwd_tile(const FwdParams &p, __bf16 *lds, const int hg, const int rb,
+                                         const int b) {
     using CF = Cfg<D>;
     constexpr int NW = Waves<D>::NW, BM = Waves<D>::BM;
     constexpr int BN = CF::BN, C8 = CF::C8, NDMA = CF::NDMA;
@@ -123,66 +146,40 @@ fwd_bf16_kernel(FwdParams p) {
     constexpr int DBLK = D / 32;    // 32-row blocks of O^T
     constexpr int KB = BN / 32;     // 32-key blocks per tile
 
-    // A 4-slot LDS ring per tensor (tile j in slot j % 4), one array per slot
-    // so that DMA in flight into one slot is visibly disjoint from reads of
-    // another; slot indices are compile-time constants in every step.
-    __shared__ __attribute__((aligned(1024))) __bf16 Ks0[BN * D];
-    __shared__ __attribute__((aligned(1024))) __bf16 Ks1[BN * D];
-    __shared__ __attribute__((aligned(1024))) __bf16 Ks2[BN * D];
-    __shared__ __attribute__((aligned(1024))) __bf16 Ks3[BN * D];
-    __shared__ __attribute__((aligned(1024))) __bf16 Vs0[BN * D];
-    __shared__ __attribute__((aligned(1024))) __bf16 Vs1[BN * D];
-    __shared__ __attribute__((aligned(1024))) __bf16 Vs2[F8 ? 8 : BN * D];  // F8: two bf16 V slots
-    __shared__ __attribute__((aligned(1024))) __bf16 Vs3[F8 ? 8 : BN * D];
-    // The workgroup's Q rows, staged once by the same direct loads (K swizzle).
-    __shared__ __attribute__((aligned(1024))) __bf16 Qs[BM * D];
+    // A 4-slot LDS ring per tensor (tile j in slot j % 4; slot indices are
+    // compile-time constants in every step), then the workgroup's Q rows,
+    // staged once by the same direct loads (K swizzle). F8: two bf16 V slots.
+    // The ring comes first so that every slot lies within the 64 KiB reach
+    // of an LDS instruction's immediate offset: one base register per lane
+    // and operand serves all slots.
+    // d = 128 bf16: two wave groups in antiphase (matrix products of one wave
+    // under the other wave's softmax on each SIMD), with 5-slot rings
+    constexpr int SLOT = Ring<D, F8>::SLOT;
+    constexpr bool PP = Ring<D, F8>::PP;
+    constexpr int NKS = Ring<D, F8>::NKS, NVS = Ring<D, F8>::NVS;
+    __bf16 *const Qs = lds + (NKS + NVS) * SLOT;
     auto kslot = [&](auto j) -> __bf16 * {
-        constexpr int J = decltype(j)::value & 3;
-        return J == 0 ? Ks0 : J == 1 ? Ks1 : J == 2 ? Ks2 : Ks3;
+        constexpr int J = decltype(j)::value % NKS;
+        return lds + J * SLOT;
     };
     auto vslot = [&](auto j) -> __bf16 * {
-        constexpr int J = decltype(j)::value & (F8 ? 1 : 3);
-        return J == 0 ? Vs0 : J == 1 ? Vs1 : J == 2 ? Vs2 : Vs3;
+        constexpr int J = decltype(j)::value % NVS;
+        return lds + (NKS + J) * SLOT;
     };
 
-    const int tid = threadIdx.x;
+    // variable length: opaque to the compiler, so that nothing derived from
+    // the lane index is hoisted out of the caller's loop over tiles and kept
+    // live across them
+    int tid = threadIdx.x;
+    if constexpr (VARLEN) asm volatile("" : "+v"(tid));
     // the wave index is wave-uniform: kept in a scalar register so that the
     // per-wave conditions below are scalar branches, not lane masks
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, half = lane >> 5;
 
-    // ---- workgroup -> (head group, row tile) ----
-    // Workgroups are dealt round-robin to the 8 XCDs (pid % 8). When the head
-    // groups split evenly over the XCDs, all row tiles of one head group run
-    // back to back on one XCD, so its K/V is fetched from HBM once and then
-    // served from that XCD's L2. Causal row tiles go heaviest first.
-    const int pid = blockIdx.x;
-    int hg, rank;
-    if ((p.n_hg & 7) == 0) {
-        const int slot = pid >> 3;
-        hg = (slot / p.n_rb) * 8 + (pid & 7);
-        rank = slot % p.n_rb;
-        if constexpr (F8 && D == 64) {
-            // A 64-byte fp8 row fills half of a 128-byte line whose other
-            // half is the same token's row of the next head group: XCD x
-            // runs head groups 16 a + 2 x and 16 a + 2 x + 1 at the same
-            // time, so both halves of each line are used from its L2.
-            if ((p.n_hg & 15) == 0) hg = (hg >> 4) * 16 + (hg & 7) * 2 + ((hg >> 3) & 1);
-        }
-    } else {
-        hg = pid / p.n_rb;
-        rank = pid % p.n_rb;
-    }
-    const int rb = CAUSAL ? (p.n_rb - 1 - rank) : rank;
     const int hpb = p.Hq / p.gpack;
     const int seq_rank = hg / hpb;
     const int qh0 = (hg - seq_rank * hpb) * p.gpack;
-    int b = seq_rank;
-    // Longest first (packed batches of 2 .. kLptMax sequences): the heaviest
-    // row tiles start first and short sequences fill the tail.
-    if constexpr (VARLEN) {
-        if (p.B > 1 && p.B <= kLptMax) b = lpt_sequence(p.cu_q, p.cu_k, p.B, seq_rank, tid);
-    }
     const int kvh = qh0 / p.G;
 
     int q_tok0, k_tok0, Lq, Lk;
@@ -431,7 +428,8 @@ fwd_bf16_kernel(FwdParams p) {
     // operand.
     auto probs = [&](const f32x16 (&sacc)[KB], bf16x8 (&pf)[KB][2], float &l_tile) {
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        l_tile = 0.f;
+        // four partial sums, so that the adds do not form one serial chain
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -439,9 +437,10 @@ fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const float pv = fast_exp2(fmaf(sacc[kb][8 * h2 + j], c, -m_use));
-                    l_tile += pv;
+                    part[j & 3] += pv;
                     pf[kb][h2][j] = (__bf16)pv;
                 }
+        l_tile = (part[0] + part[1]) + (part[2] + part[3]);
     };
     // O^T += V^T P^T. P^T key order in lane (col, half) for k-slot j:
     // key = kb*32 + 16*h2 + 8*(j/4) + 4*half + j%4, matched by the V^T reads.
@@ -484,6 +483,151 @@ fwd_bf16_kernel(FwdParams p) {
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
+
+    if constexpr (PP) {
+        // ---- Two wave groups in antiphase (d = 128, bf16) ----
+        // Waves w and w + 4 share a SIMD. Group 0 (waves 0-3) and group 1
+        // (waves 4-7) run the same sequence of two clusters per K/V tile t:
+        //   C(t): the LDS reads of K(t+1) (the A operand of S(t+1)), the
+        //         products O~ += V(t)^T P(t) while they arrive, then
+        //         S(t+1) = K(t+1) Q^T;
+        //   X(t): the DMA of K(t+5) and V(t+4), the probabilities
+        //         P(t+1) = 2^(S(t+1) c - m) and their sum, and the transposing
+        //         LDS reads of V(t+1) for the next cluster,
+        // with a workgroup barrier after each cluster. Group 1 passes one
+        // barrier more at the start, so between two barriers one wave of each
+        // SIMD issues matrix instructions while the other issues vector
+        // instructions, and both issue LDS reads (a wave's LDS reads are
+        // served at a limited rate, so the reads are split between them).
+        //
+        // Ring safety (5 slots per tensor; barrier b ends interval b; group 0
+        // runs C(t) in interval 2t+1 and X(t) in 2t+2, group 1 X(t-1) in 2t+1
+        // and C(t) in 2t+2): K(j) is read in intervals 2j-1 and 2j, V(j) in
+        // 2j and 2j+1; the DMA of K(j+5) and V(j+5) into their slots is
+        // issued in X(j) and X(j+1) (intervals >= 2j+2). Each group waits at
+        // the end of X(t) for its loads issued in X(t-2) (vmcnt(4): the two
+        // latest groups of one K and one V load stay in flight), so K(j) has
+        // landed in both groups' shares by barrier 2j-3 and V(j) by 2j-1.
+        const bool lag = wave >= NW / 2;  // wave-uniform
+        bf16x8 kf[DSTEPS];                // K(t+1), the A operand of S(t+1)
+        bf16x8 vfr[KB][2][DBLK];          // V(t)^T operand
+        bf16x8 pfr[KB][2];                // P(t) in bf16
+        f32x16 sc[KB];                    // S(t+1)
+        auto read_k = [&](const __bf16 *ks) {
+#pragma unroll
+            for (int s = 0; s < DSTEPS; ++s) kf[s] = *(const bf16x8 *)(ks + k_rd[s]);
+        };
+        auto score_products = [&] {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                sc[kb] = f32x16{};
+#pragma unroll
+                for (int s = 0; s < DSTEPS; ++s)
+                    sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], sc[kb], 0, 0, 0);
+            }
+        };
+        auto cluster_barrier = [] {
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_barrier" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto data_barrier = [] {  // two latest DMA groups may stay in flight
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto cluster_c = [&](auto jc, int t) {
+            constexpr int J = decltype(jc)::value;
+            __builtin_amdgcn_s_setprio(2);
+            const bool more = t + 1 < ntiles;  // wave-uniform
+            if (more) read_k(kslot(std::integral_constant<int, J + 1>{}));
+            accumulate(vfr, pfr);
+            if (more) score_products();
+            __builtin_amdgcn_s_setprio(0);
+        };
+        auto cluster_x = [&](auto jc, int t) {
+            constexpr int J = decltype(jc)::value;
+            if (t + 1 < ntiles) {
+                dma_k(t + 5, kslot(std::integral_constant<int, J + 5>{}));
+                dma_v(t + 4, vslot(std::integral_constant<int, J + 4>{}));
+                mask(t + 1, sc);
+                float l_tile;
+                load_v(vslot(std::integral_constant<int, J + 1>{}), vfr);
+                probs(sc, pfr, l_tile);
+                if (__builtin_amdgcn_ballot_w64(l_tile > kTileSumBound)) {
+                    raise_max(sc);
+                    probs(sc, pfr, l_tile);
+                }
+                l_run += l_tile;
+                data_barrier();
+            }
+        };
+        auto pp_step = [&](auto jc, int t) {
+            cluster_c(jc, t);
+            if (t == 0 && !lag) {
+                data_barrier();  // K(2), V(1) have landed
+            } else {
+                cluster_barrier();
+            }
+            cluster_x(jc, t);
+        };
+        using I4 = std::integral_constant<int, 4>;
+        if (ntiles > 0) {
+            constexpr int NQ = BM * D * 2 / 1024 / NW;  // Q loads per wave
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const int idx = 64 * (wave + NW * i) + lane;
+                const int r = idx / C8;
+                const int rho = min(row0 + r, rows_total - 1);
+                const int qp = rho / p.gpack;
+                const int qh = qh0 + (rho - qp * p.gpack);
+                const __bf16 *src = (const __bf16 *)p.q + ((int64_t)(q_tok0 + qp) * p.Hq + qh) * D +
+                                    ((idx % C8) ^ CF::swz_k(r)) * 8;
+                lds_dma16(src, lds_addr(Qs) + 1024 * (wave + NW * i));
+            }
+            dma_k(0, kslot(I0{}));
+            dma_k(1, kslot(I1{}));
+            dma_v(0, vslot(I0{}));
+            dma_k(2, kslot(I2{}));
+            dma_v(1, vslot(I1{}));
+            dma_k(3, kslot(I3{}));
+            dma_v(2, vslot(I2{}));
+            dma_k(4, kslot(I4{}));
+            dma_v(3, vslot(I3{}));
+            // Q, K(0), K(1), V(0) have landed (K(2) .. V(3) may not)
+            asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+            for (int s = 0; s < DSTEPS; ++s) qf[s] = *(const bf16x8 *)(Qs + wave * 32 * D + k_rd[s]);
+            read_k(kslot(I0{}));
+            score_products();
+            load_v(vslot(I0{}), vfr);
+            mask(0, sc);
+            raise_max(sc);
+            {
+                float l_tile;
+                probs(sc, pfr, l_tile);
+                l_run += l_tile;
+            }
+            if (lag) data_barrier();  // group 1 starts one cluster behind
+            int t = 0;
+            for (; t + 4 < ntiles; t += 5) {
+                pp_step(I0{}, t);
+                pp_step(I1{}, t + 1);
+                pp_step(I2{}, t + 2);
+                pp_step(I3{}, t + 3);
+                pp_step(I4{}, t + 4);
+            }
+            if (t < ntiles) pp_step(I0{}, t);
+            if (t + 1 < ntiles) pp_step(I1{}, t + 1);
+            if (t + 2 < ntiles) pp_step(I2{}, t + 2);
+            if (t + 3 < ntiles) pp_step(I3{}, t + 3);
+            // Group 1 has passed one barrier more (at the start): group 0
+            // passes one more here, so that both leave the tile with the same
+            // count and a later workgroup barrier (the next tile's) meets
+            // every wave at the same point.
+            if (!lag) cluster_barrier();
+        }
+    } else {
     f32x16 sa[KB], sb[KB];
     if (ntiles > 0 && F8) {
         // fp8 Q rows (D bytes each, swizzled as the K rows), then KV(0..3)
@@ -619,6 +763,7 @@ fwd_bf16_kernel(FwdParams p) {
     if (t < ntiles) step(I0{}, t, sa, sb);
     if (t + 1 < ntiles) step(I1{}, t + 1, sb, sa);
     if (t + 2 < ntiles) step(I2{}, t + 2, sa, sb);
+    }
     // drain this wave's remaining (unused) DMA before the workgroup can end
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -657,8 +802,7 @@ fwd_bf16_kernel(FwdParams p) {
             *(u32x4 *)((__bf16 *)p.o + ((int64_t)(q_tok0 + rp) * p.Hq + rh) * D + c * 8) = v;
         }
     }
-    if (!row_ok) return;
-    if (half == 0) {
+    if (row_ok && half == 0) {
         const float lse = empty ? -INFINITY : (m_run + __log2f(l_tot)) * kLn2;
         const int64_t li = VARLEN ? (int64_t)(q_tok0 + pos) * p.Hq + head
                                   : ((int64_t)b * p.Hq + head) * p.Sq + pos;
@@ -666,12 +810,248 @@ fwd_bf16_kernel(FwdParams p) {
     }
 }
 
+// ---- Workgroup scheduling ----
+// One tile per workgroup (p.persist 0): workgroup pid takes one row tile.
+// Workgroups are dealt round-robin to the 8 XCDs (pid mod 8); when the head
+// groups split evenly over the XCDs, all row tiles of one head group run back
+// to back on one XCD, so its K/V is fetched from HBM once and then served
+// from that XCD's L2. Causal row tiles go heaviest first, and packed batches
+// of 2 .. kLptMax sequences longest first.
+//
+// Persistent (p.persist 1; variable length): the grid is the number of
+// workgroups the device holds at once, and each workgroup claims row tiles
+// until none is left, so that no workgroup start or end (a few microseconds
+// each: the outstanding stores drain and the next workgroup is dispatched)
+// separates two tiles, no workgroup is spent on an empty tile of a short
+// sequence, and the last tiles go to whichever workgroups are free. With 8
+// lists (head groups divisible by 8), list x holds the row tiles of the head
+// groups that the one-tile order sends to XCD x, head group by head group,
+// each heaviest first, and workgroup w starts on list w mod 8 (its XCD under
+// round-robin dispatch, so that the tiles of one head group share that XCD's
+// L2). A tile is claimed by an atomic add on its list's counter p.sched[x]
+// (agent scope) after the previous tile ends (claiming one ahead did not
+// help: the tile's own in-order load waits then wait for the atomic too);
+// once its own list is empty a workgroup moves on to the next. p.sched[8]
+// counts the workgroups that have finished; the last one returns the nine
+// counters to zero for the next launch that uses the same slot. The live row
+// tiles of every head group (ceil(G Lq / BM), none for an empty sequence) are
+// counted and prefix-summed per list in LDS at the start; with more than
+// kPersistMaxHg head groups every head group keeps n_rb entries and the empty
+// ones end at once. Fixed-length shapes keep one tile per workgroup: there,
+// persistent workgroups measured no faster (causal) or slower (the encoder,
+// whose equal tiles then start in lockstep).
+constexpr int kSchedSlots = 64;     // launches in flight per device that may share no slot
+constexpr int kPersistMaxHg = 1024;  // variable length: head groups the LDS prefix holds
+__device__ unsigned int g_fwd_sched[kSchedSlots][16];  // zero at load; each launch leaves its slot at zero
+
+// Head group of entry j of list `list` (8 lists: the XCD order above).
+template <int D, bool F8>
+__device__ __forceinline__ int hg_of(const FwdParams &p, int list, int j, bool xcd) {
+    if (!xcd) return j;
+    int hg = 8 * j + list;
+    if constexpr (F8 && D == 64) {
+        // A 64-byte fp8 row fills half of a 128-byte line whose other half is
+        // the same token's row of the next head group: XCD x runs head groups
+        // 16 a + 2 x and 16 a + 2 x + 1 at the same time, so both halves of
+        // each line are used from its L2.
+        if ((p.n_hg & 15) == 0) hg = (hg >> 4) * 16 + (hg & 7) * 2 + ((hg >> 3) & 1);
+    }
+    return hg;
+}
+
 template <int D, bool CAUSAL, bool VARLEN, bool F8>
-hipError_t launch_t(const FwdParams &p, hipStream_t s) {
-    const long long grid = (long long)p.n_hg * p.n_rb;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, VARLEN, F8>), dim3((unsigned)grid),
-                       dim3(Waves<D>::NTHREADS), 0,
-                       s, p);
+__global__ __launch_bounds__(Waves<D>::NTHREADS) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2))) void
+fwd_bf16_kernel(FwdParams p) {
+    constexpr int BM = Waves<D>::BM, NW = Waves<D>::NW;
+    __shared__ __attribute__((aligned(1024))) __bf16 lds[Ring<D, F8>::ELEMS];
+    __shared__ long long s_work[kLptMax];
+    __shared__ int s_order[kLptMax];           // sequence of longest-first rank r
+    __shared__ int s_pref[kPersistMaxHg + 8];  // per list: prefix of live row tiles
+    __shared__ int s_ctl[3];                   // claimed item, its list, lists not yet found empty
+    const int tid = threadIdx.x;
+    if constexpr (!VARLEN) {
+        // one row tile per workgroup
+        const int pid = blockIdx.x;
+        const bool xcd = (p.n_hg & 7) == 0;
+        const int slot = xcd ? pid >> 3 : pid;
+        const int j = slot / p.n_rb, rank = slot - j * p.n_rb;
+        const int hg = hg_of<D, F8>(p, xcd ? pid & 7 : 0, j, xcd);
+        fwd_tile<D, CAUSAL, VARLEN, F8>(p, lds, hg, CAUSAL ? (p.n_rb - 1 - rank) : rank, hg / (p.Hq / p.gpack));
+        return;
+    }
+    const int mode = p.persist;
+    const bool xcd = (p.n_hg & 7) == 0;
+    const int nl = xcd ? 8 : 1;
+    const int per_list = p.n_hg / nl;
+    const bool lpt = VARLEN && p.B > 1 && p.B <= kLptMax;
+    // dense lists of live row tiles (persistent, variable length); otherwise
+    // every head group has n_rb entries and the empty ones end at once
+    const bool dense = VARLEN && mode != 0 && p.n_hg <= kPersistMaxHg;
+    if (lpt) {
+        if (tid < p.B) s_work[tid] = (long long)(p.cu_q[tid + 1] - p.cu_q[tid]) * (p.cu_k[tid + 1] - p.cu_k[tid]);
+        __syncthreads();
+        if (tid < p.B) {
+            const long long mine = s_work[tid];
+            int r = 0;
+            for (int y = 0; y < p.B; ++y) r += (s_work[y] > mine) || (s_work[y] == mine && y < tid);
+            s_order[r] = tid;
+        }
+    }
+    if (dense) {
+        // wave w counts and scans lists w, w + NW, ...
+        if (lpt) __syncthreads();
+        const int lane = tid & 63, wave = tid >> 6;
+        for (int l = wave; l < nl; l += NW) {
+            int *pf = s_pref + l * (per_list + 1);
+            if (lane == 0) pf[0] = 0;
+            int carry = 0;
+            for (int j0 = 0; j0 < per_list; j0 += 64) {
+                const int j = j0 + lane;
+                int x = 0;
+                if (j < per_list) {
+                    const int r = hg_of<D, F8>(p, l, j, xcd) / (p.Hq / p.gpack);
+                    const int bb = lpt ? s_order[r] : r;
+                    x = ((p.cu_q[bb + 1] - p.cu_q[bb]) * p.gpack + BM - 1) / BM;
+                }
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int y = __shfl_up(x, off);
+                    if (lane >= off) x += y;
+                }
+                if (j < per_list) pf[j + 1] = carry + x;
+                carry += __shfl(x, 63);
+            }
+        }
+    }
+    if (tid == 0) {
+        const int l0 = xcd ? (int)(blockIdx.x & 7) : 0;
+        s_ctl[0] = mode ? (int)atomicAdd(&p.sched[l0], 1u) : (int)(xcd ? blockIdx.x >> 3 : blockIdx.x);
+        s_ctl[1] = l0;
+        s_ctl[2] = mode ? nl : 1;
+    }
+    __syncthreads();
+    // Between tiles the scheduling state lives in LDS and the launch
+    // parameters are re-read from the kernel argument segment (p is its only
+    // argument, at offset 0) through an opaque copy of its address, so that
+    // only that address stays in scalar registers across a tile, which needs
+    // nearly all of them.
+    for (;;) {
+        typedef const __attribute__((address_space(4))) FwdParams *KernargPtr;
+        KernargPtr pp = (KernargPtr)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(pp));
+        const FwdParams &q = *(const FwdParams *)pp;
+        const bool xq = (q.n_hg & 7) == 0;
+        const int nq = xq ? 8 : 1, per = q.n_hg / nq, hpq = q.Hq / q.gpack;
+        const bool lq = VARLEN && q.B > 1 && q.B <= kLptMax;
+        const bool pq = VARLEN && q.persist != 0;
+        const bool dq = pq && q.n_hg <= kPersistMaxHg;
+        auto n_items = [&](int l) {
+            return dq ? __builtin_amdgcn_readfirstlane(s_pref[l * (per + 1) + per]) : per * q.n_rb;
+        };
+        int item = __builtin_amdgcn_readfirstlane(s_ctl[0]);
+        int list = __builtin_amdgcn_readfirstlane(s_ctl[1]);
+        int left = __builtin_amdgcn_readfirstlane(s_ctl[2]);
+        while (item >= n_items(list) && left > 1) {
+            --left;
+            list = list + 1 == nq ? 0 : list + 1;
+            __syncthreads();  // every thread has read s_ctl
+            if (tid == 0) s_ctl[0] = (int)atomicAdd(&q.sched[list], 1u);
+            __syncthreads();
+            item = __builtin_amdgcn_readfirstlane(s_ctl[0]);
+        }
+        if (left == 0 || item >= n_items(list)) break;
+        int j, rank, nrb = q.n_rb;
+        if (dq) {
+            const int *pf = s_pref + list * (per + 1);
+            int lo = 0, hi = per;  // pf[lo] <= item < pf[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (__builtin_amdgcn_readfirstlane(pf[mid]) <= item) lo = mid; else hi = mid;
+            }
+            j = lo;
+            rank = item - __builtin_amdgcn_readfirstlane(pf[j]);
+            nrb = __builtin_amdgcn_readfirstlane(pf[j + 1]) - (item - rank);
+        } else {
+            j = item / q.n_rb;
+            rank = item - j * q.n_rb;
+        }
+        const int hg = hg_of<D, F8>(q, list, j, xq);
+        const int r = hg / hpq;
+        const int b = lq ? __builtin_amdgcn_readfirstlane(s_order[r]) : r;
+        fwd_tile<D, CAUSAL, VARLEN, F8>(q, lds, hg, CAUSAL ? (nrb - 1 - rank) : rank, b);
+        __syncthreads();  // the tile's use of the LDS has ended everywhere
+        if (tid == 0) {
+            s_ctl[0] = pq ? (int)atomicAdd(&q.sched[list], 1u) : -1;
+            s_ctl[1] = list;
+            s_ctl[2] = pq ? left : 0;
+        }
+        __syncthreads();
+    }
+    if (mode && tid == 0) {
+        const unsigned int done = atomicAdd(&p.sched[8], 1u);
+        if (done == gridDim.x - 1)
+            for (int i = 0; i < 9; ++i) atomicExch(&p.sched[i], 0u);
+    }
+}
+
+bool persistent_enabled() {
+    static const bool on = [] {
+        const char *e = std::getenv("GQA_FWD_PERSISTENT");
+        return !(e && e[0] == '0');
+    }();
+    return on;
+}
+
+constexpr int kMaxDevices = 64;
+
+// The next scheduling slot of the current device (slots rotate over
+// kSchedSlots launches), or null if its address cannot be obtained.
+unsigned int *sched_slot() {
+    static std::mutex mu;
+    static unsigned int *base[kMaxDevices] = {};
+    static std::atomic<unsigned int> next[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (!base[dev]) {
+            void *ptr = nullptr;
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_fwd_sched)) != hipSuccess || !ptr) return nullptr;
+            base[dev] = static_cast<unsigned int *>(ptr);
+        }
+    }
+    return base[dev] + 16 * (next[dev].fetch_add(1, std::memory_order_relaxed) % kSchedSlots);
+}
+
+template <int D, bool CAUSAL, bool VARLEN, bool F8>
+hipError_t launch_t(FwdParams p, hipStream_t s) {
+    auto kernel = fwd_bf16_kernel<D, CAUSAL, VARLEN, F8>;
+    long long grid = (long long)p.n_hg * p.n_rb;
+    p.persist = 0;
+    p.sched = nullptr;
+    if (VARLEN && persistent_enabled()) {
+        // workgroups the device holds at once (per device, computed once)
+        static std::atomic<int> resident[kMaxDevices];
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+            int cap = resident[dev].load(std::memory_order_relaxed);
+            if (cap == 0) {
+                int per_cu = 0, cus = 0;
+                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, Waves<D>::NTHREADS, 0) ==
+                        hipSuccess &&
+                    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+                    cap = per_cu * cus;
+                resident[dev].store(cap, std::memory_order_relaxed);
+            }
+            unsigned int *slot = cap > 0 ? sched_slot() : nullptr;
+            if (slot) {
+                p.persist = 1;
+                p.sched = slot;
+                grid = std::min<long long>(grid, cap);
+            }
+        }
+    }
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(Waves<D>::NTHREADS), 0, s, p);
     return hipGetLastError();
 }
 

@@ -30,6 +30,11 @@ struct FwdParams {
     int split_chunk;
     float *ws_o;
     float *ws_lse;
+    // bf16 / fp8 kernel scheduling: 0 one row tile per workgroup; 1
+    // persistent, tiles claimed through the counters at sched (nine unsigned
+    // ints, zero on entry and on exit)
+    int persist;
+    unsigned int *sched;
 };
 
 // One split-KV decode launch (bf16 queries; bf16 or fp8 e4m3 K/V cache).

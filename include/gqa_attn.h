@@ -87,6 +87,15 @@ enum {
  * Requirements: B, Hq, Hkv >= 1; Sq, Sk >= 1 for fixed length and >= 0 for
  * variable length; Hq % Hkv == 0; Hkv * d <= 4194304 (one token's K row at
  * most 8 MiB, so per-lane offsets inside a key tile fit 24 bits).
+ * Scheduling (bf16 and fp8, variable length): one workgroup per resident
+ * slot of the device takes row tiles until none is left, claiming them
+ * through nine counters in device memory that the library holds (64 such
+ * slots per device, used in turn by successive calls; every call returns its
+ * slot to zero). Calls whose executions overlap on one device must not share
+ * a slot, so at most 64 variable-length forward calls may be executing on
+ * one device at a time. Setting the environment variable
+ * GQA_FWD_PERSISTENT=0 before the first call launches one workgroup per row
+ * tile instead (as fixed-length calls always do).
  */
 int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
                  int B, int Hq, int Hkv, int Sq, int Sk, int d, float scale, int causal,

@@ -250,6 +250,37 @@ def test_varlen_many_sequences(causal):
         compare(o, l, *oracle_fwd(w), torch.bfloat16, f"varlen {n} sequences")
 
 
+def test_varlen_beyond_the_dense_tile_lists():
+    """1040 head groups (520 sequences x 2 K/V heads): more than the LDS list of
+    live tiles holds, so every head group keeps its max-length row-tile count
+    and the empty tiles end at once; lengths 0 .. 40 with many empty ones."""
+    g = torch.Generator().manual_seed(41)
+    lens = torch.randint(0, 41, (520,), generator=g)
+    lens[::7] = 0
+    lens = lens.tolist()
+    for causal in (True, False):
+        w = gqa_inputs.varlen(lens, lens, 4, 2, 64, seed=42, causal=causal)
+        o, l = run_fwd(w)
+        compare(o, l, *oracle_fwd(w), torch.bfloat16, f"varlen 1040 head groups causal={causal}")
+
+
+def test_varlen_calls_reuse_scheduling_slots():
+    """Seventy variable-length calls in a row (more than the 64 counter slots
+    they take in turn), alternating two shapes: every call of a shape returns
+    the same bits, and the first of each matches the oracle."""
+    a = gqa_inputs.varlen([300, 0, 45, 1000], [300, 0, 45, 1000], 32, 8, 128, seed=43, causal=True)
+    b = gqa_inputs.varlen([7, 513], [900, 513], 8, 8, 64, seed=44, causal=False)
+    firsts = {}
+    for i in range(70):
+        w = a if i % 2 == 0 else b
+        o, l = run_fwd(w)
+        if i < 2:
+            firsts[i] = (o, l)
+            compare(o, l, *oracle_fwd(w), torch.bfloat16, f"slot reuse {i}")
+        else:
+            assert torch.equal(o, firsts[i % 2][0]) and torch.equal(l, firsts[i % 2][1]), i
+
+
 def test_empty_varlen_batch():
     w = gqa_inputs.varlen([0, 0], [0, 5], 4, 2, 64, seed=13)
     o, l = ga.fwd(w.q.cuda(), w.k.cuda(), w.v.cuda(), cu_seqlens_q=w.cu_seqlens_q.cuda(),
