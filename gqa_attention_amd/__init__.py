@@ -42,7 +42,9 @@ __all__ = ["fwd", "fwd_fp8", "bwd", "decode", "decode_ex", "FwdPlan", "BwdPlan",
            "GQA_OK", "GQA_EINVAL", "GQA_EUNSUPPORTED", "GQA_EWORKSPACE", "GQA_ELAUNCH",
            "GQA_DTYPE_BF16", "GQA_DTYPE_FP32", "GQA_DTYPE_FP8_E4M3", "GqaError"]
 
-GQA_OK, GQA_EINVAL, GQA_EUNSUPPORTED, GQA_EWORKSPACE, GQA_ELAUNCH = 0, 1, 2, 3, 4
+GQA_OK, GQA_EINVAL, GQA_EUNSUPPORTED, GQA_EWORKSPACE, GQA_ELAUNCH, GQA_ESCRATCH = 0, 1, 2, 3, 4, 5
+# bytes of the static device scratch behind decode_noalloc (per GPU)
+NOALLOC_SCRATCH_BYTES = 16 << 20
 GQA_DTYPE_BF16, GQA_DTYPE_FP32, GQA_DTYPE_FP8_E4M3 = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -82,6 +84,9 @@ def lib() -> ctypes.CDLL:
     L.gqa_attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz,
                                   i32, vp]
     L.gqa_attn_decode.restype = i32
+    L.gqa_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
+                                          i32, vp]
+    L.gqa_attn_decode_noalloc.restype = i32
     L.gqa_attn_decode_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, i32, vp,
                                      i32, i32, i32, i32, f32, f32, i32, vp, sz, vp]
     L.gqa_attn_decode_ex.restype = i32
@@ -401,6 +406,23 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *,
     with torch.cuda.device(q.device):
         st = lib().gqa_attn_decode(*args, _stream_handle(q.device))
     _raise(st, "gqa_attn_decode")
+    return out, lse
+
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *,
+                   scale: Optional[float] = None, num_splits: int = 1,
+                   out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Split-KV decode through ``gqa_attn_decode_noalloc``: the library's
+    static device scratch holds the split partials, so the call itself
+    allocates nothing (pass ``out`` and ``lse`` to allocate nothing here
+    either). Same layouts and results as ``decode``; calls that overlap on
+    one GPU race on the shared scratch."""
+    out, lse, _, args = _prepare_decode(q, k_cache, v_cache, scale, 1, None, out, lse)
+    args = args[:11] + (int(num_splits), args[14])
+    with torch.cuda.device(q.device):
+        st = lib().gqa_attn_decode_noalloc(*args, _stream_handle(q.device))
+    _raise(st, "gqa_attn_decode_noalloc")
     return out, lse
 
 

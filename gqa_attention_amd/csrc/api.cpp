@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
@@ -43,6 +44,31 @@ void split_workspace(void *workspace, int B, int Hq, int d, int num_splits, floa
                                        gqa::decode_workspace_o_bytes(B, Hq, d, num_splits));
 }
 
+// Static scratch of gqa_attn_decode_noalloc: the split partials of callers
+// that cannot allocate. Every GPU the library runs on holds its own copy
+// until the process ends. In host code the name `scratch` is only a stand-in
+// for the symbol: its device address (different on every GPU) comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+__device__ __align__(256) unsigned char scratch[GQA_ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, or null if it cannot be
+// obtained.
+void *scratch_address() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -54,6 +80,7 @@ const char *gqa_attn_strerror(int status) {
         case GQA_EUNSUPPORTED: return "unsupported head_dim or dtype";
         case GQA_EWORKSPACE: return "decode workspace missing or too small";
         case GQA_ELAUNCH: return "kernel launch failed";
+        case GQA_ESCRATCH: return "decode partials exceed the static scratch buffer";
         default: return "unknown status";
     }
 }
@@ -263,6 +290,26 @@ int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache, voi
     if (e != hipSuccess) return status_from(e);
     return status_from(
         gqa::launch_decode_combine(ws_o, ws_lse, out, lse, rows, num_splits, d, false, s));
+}
+
+int gqa_attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache, void *out,
+                            float *lse, int B, int Hq, int Hkv, int Sk, int d, float scale,
+                            int num_splits, int dtype, void *stream) {
+    // the same checks as gqa_attn_decode with a workspace of the scratch's
+    // size (a stand-in pointer: nothing is launched before they pass)
+    const int rc = gqa::validate_decode(q, k_cache, v_cache, out, lse, B, Hq, Hkv, Sk, d, scale,
+                                        num_splits, reinterpret_cast<void *>(uintptr_t(256)),
+                                        (size_t)GQA_ATTN_NOALLOC_SCRATCH_BYTES, dtype);
+    if (rc == GQA_EWORKSPACE) return GQA_ESCRATCH;
+    if (rc != GQA_OK) return rc;
+    void *ws = nullptr;
+    if (num_splits > 1) {
+        ws = scratch_address();
+        if (!ws) return GQA_ELAUNCH;
+    }
+    return gqa_attn_decode(q, k_cache, v_cache, out, lse, B, Hq, Hkv, Sk, d, scale, num_splits,
+                           ws, num_splits > 1 ? (size_t)GQA_ATTN_NOALLOC_SCRATCH_BYTES : 0, dtype,
+                           stream);
 }
 
 int gqa_attn_decode_ex(const void *q, const void *k_cache, const void *v_cache, void *out,

@@ -65,8 +65,12 @@ enum {
     GQA_EINVAL = 1,        /* bad argument: null pointer, bad size, head ratio, scale, alignment */
     GQA_EUNSUPPORTED = 2,  /* head_dim not in {64, 128} or unknown dtype */
     GQA_EWORKSPACE = 3,    /* decode workspace NULL or too small for num_splits > 1 */
-    GQA_ELAUNCH = 4        /* the HIP runtime refused a kernel launch */
+    GQA_ELAUNCH = 4,       /* the HIP runtime refused a kernel launch */
+    GQA_ESCRATCH = 5       /* gqa_attn_decode_noalloc: partials larger than its static scratch */
 };
+
+/* Bytes of the static device scratch behind gqa_attn_decode_noalloc (per GPU). */
+#define GQA_ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /*
  * gqa_attn_fwd - exact attention forward (prefill / encoder), fixed length or
@@ -197,6 +201,32 @@ int gqa_attn_decode(const void *q, const void *k_cache, const void *v_cache, voi
                     float *lse, int B, int Hq, int Hkv, int Sk, int d, float scale,
                     int num_splits, void *workspace, size_t workspace_bytes,
                     int dtype, void *stream);
+
+/*
+ * gqa_attn_decode_noalloc - gqa_attn_decode without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. It allocates nothing
+ * (no hipMalloc, hipFree or allocating library call); the caller passes the
+ * inputs and outputs exactly as for gqa_attn_decode, and for num_splits > 1
+ * the fp32 split partials go to a static device array of
+ * GQA_ATTN_NOALLOC_SCRATCH_BYTES bytes (16 MiB) that the library holds on
+ * every GPU it runs on until the process ends (its address is looked up once
+ * per device, on the first call with that device current). Nothing in it must
+ * start at zero: every split writes its LSE (-inf when empty) and the merge
+ * reads a split's O only when its LSE is finite.
+ * Limit: gqa_attn_decode_workspace_bytes(B, Hq, d, num_splits) must not exceed
+ * GQA_ATTN_NOALLOC_SCRATCH_BYTES (B * Hq * (d + 1) * 4 * num_splits bytes,
+ * rounded; e.g. B 64, Hq 32, d 128, num_splits 8 needs 8.5 MB), else
+ * GQA_ESCRATCH before anything is launched. num_splits == 1 uses no scratch.
+ * All calls on one GPU share its scratch, which keeps the last call's
+ * contents: calls that overlap on one GPU (different streams, or different
+ * host threads without ordering) race; issue them on one stream.
+ * Errors: as gqa_attn_decode (GQA_EWORKSPACE cannot occur), GQA_ESCRATCH, and
+ * GQA_ELAUNCH also when the scratch address cannot be obtained.
+ */
+int gqa_attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache, void *out,
+                            float *lse, int B, int Hq, int Hkv, int Sk, int d, float scale,
+                            int num_splits, int dtype, void *stream);
 
 /*
  * gqa_attn_decode_ex - decode over a ragged, optionally paged, optionally

@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_the_api():
     assert declared_functions() == ["gqa_attn_bwd", "gqa_attn_bwd_workspace_bytes",
                                     "gqa_attn_decode", "gqa_attn_decode_ex",
-                                    "gqa_attn_decode_num_splits",
+                                    "gqa_attn_decode_noalloc", "gqa_attn_decode_num_splits",
                                     "gqa_attn_decode_workspace_bytes", "gqa_attn_fwd",
                                     "gqa_attn_fwd_fp8", "gqa_attn_strerror"]
 
@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol():
 @needs_lib
 def test_strerror():
     assert ga.strerror(0) == "success"
-    for s in (1, 2, 3, 4):
+    for s in (1, 2, 3, 4, 5):
         assert ga.strerror(s) and ga.strerror(s) != "unknown status"
     assert ga.strerror(99) == "unknown status"
 
@@ -328,3 +328,26 @@ def test_bwd_workspace_size():
     assert bwd_call(ws_bytes=need - 1) == ga.GQA_EWORKSPACE
     need = f(1, 32, 1, 8192, 8192, 128)
     assert bwd_call(B=1, Hq=32, Hkv=1, Sq=8192, Sk=8192, ws_bytes=need - 1) == ga.GQA_EWORKSPACE
+
+
+def noalloc_call(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, B=2, Hq=8, Hkv=2, Sk=100, d=128,
+             scale=0.1, ns=4, dtype=0, stream=None)
+    a.update(kw)
+    return ga.lib().gqa_attn_decode_noalloc(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"],
+                                            a["Hq"], a["Hkv"], a["Sk"], a["d"], a["scale"],
+                                            a["ns"], a["dtype"], a["stream"])
+
+
+@needs_lib
+def test_noalloc_decode_host_errors():
+    """The static-scratch decode checks its arguments like gqa_attn_decode and
+    rejects partials larger than its scratch, all before any launch."""
+    assert noalloc_call(q=None) == ga.GQA_EINVAL
+    assert noalloc_call(ns=0) == ga.GQA_EINVAL
+    assert noalloc_call(d=96) == ga.GQA_EUNSUPPORTED
+    # 1024 x 64 heads x (128 + 1) floats x 64 splits: 2.2 GB > 16 MiB
+    assert noalloc_call(B=1024, Hq=64, Hkv=8, Sk=4096, ns=64) == ga.GQA_ESCRATCH
+    assert ga.decode_workspace_bytes(1024, 64, 128, 64) > ga.NOALLOC_SCRATCH_BYTES
+    # the largest decode-workload shape it is meant for fits: B 64, 32 heads, d 128, 8 splits
+    assert ga.decode_workspace_bytes(64, 32, 128, 8) <= ga.NOALLOC_SCRATCH_BYTES
