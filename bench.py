@@ -394,6 +394,60 @@ WORKLOAD_NAMES = {
 }
 
 
+def split_sweep(torch, ga):
+    """Decode time at num_splits 1, 2, 4, 8, 16 for contiguous bf16 caches
+    (Llama heads: 32 query, 8 K/V heads), B 1..128, 512..32768 keys, d 64 and
+    128, against the count gqa_attn_decode_num_splits picks. Each time is the
+    smallest of three averages over 20 back-to-back launches, after a warm-up
+    that lets the clocks ramp. Prints a markdown table and a summary line."""
+    Hq, Hkv = 32, 8
+    counts = (1, 2, 4, 8, 16)
+    rows, worst = [], 1.0
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    for d in (64, 128):
+        for Sk in (512, 2048, 8192, 32768):
+            for B in (1, 2, 4, 8, 16, 32, 64, 128):
+                q = torch.randn(B, Hq, d, device="cuda", generator=gen).to(torch.bfloat16)
+                k = torch.randn(B, Sk, Hkv, d, device="cuda", generator=gen).to(torch.bfloat16)
+                v = torch.randn(B, Sk, Hkv, d, device="cuda", generator=gen).to(torch.bfloat16)
+                times = {}
+                for ns in counts:
+                    plan = ga.DecodePlan(q, k, v, num_splits=ns)
+                    t_end = time.perf_counter() + 0.03
+                    while time.perf_counter() < t_end:
+                        plan.run()
+                        torch.cuda.synchronize()
+                    best = float("inf")
+                    for _ in range(3):
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record()
+                        for _ in range(20):
+                            plan.run()
+                        e1.record()
+                        torch.cuda.synchronize()
+                        best = min(best, e0.elapsed_time(e1) / 20)
+                    times[ns] = best
+                pick = ga.decode_num_splits(B, Hq, Hkv, d, Sk)
+                fastest = min(times, key=times.get)
+                ratio = times[fastest] / times[pick]
+                worst = min(worst, ratio)
+                gbs = 2 * k.numel() * 2 / (times[pick] * 1e-3) / 1e9
+                rows.append((d, Sk, B, times, pick, fastest, ratio, gbs))
+                del q, k, v
+                torch.cuda.empty_cache()
+    print("| d | keys | B | " + " | ".join(f"ns={c} µs" for c in counts) +
+          " | best | picked | best/picked time | picked GB/s |")
+    print("|---" * (len(counts) + 7) + "|")
+    for d, Sk, B, times, pick, fastest, ratio, gbs in rows:
+        print(f"| {d} | {Sk} | {B} | " + " | ".join(f"{times[c] * 1e3:.1f}" for c in counts) +
+              f" | {fastest} | {pick} | {ratio:.3f} | {gbs:.0f} |")
+    ratios = [r[6] for r in rows]
+    print(json.dumps({"points": len(rows), "picked_is_best": sum(r[4] == r[5] for r in rows),
+                      "worst_best_over_picked": round(worst, 4),
+                      "median_best_over_picked": round(float(sorted(ratios)[len(ratios) // 2]), 4)}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -419,6 +473,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-counters", metavar="PMC_DIR",
                     help="write profiles/hbm_traffic.json from rocprofv3 counter runs and exit")
+    ap.add_argument("--split-sweep", action="store_true",
+                    help="time gqa_attn_decode at every split count over a grid of contiguous "
+                         "bf16 caches, compare with gqa_attn_decode_num_splits (markdown table) "
+                         "and exit")
     args = ap.parse_args()
 
     if args.summarize_counters:
@@ -440,6 +498,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     ga.lib()  # fail loudly if the HIP library is missing
+
+    if args.split_sweep:
+        split_sweep(torch, ga)
+        return
 
     # secondary workloads: warm up until the clocks have ramped, then time
     # about 20 ms of launches

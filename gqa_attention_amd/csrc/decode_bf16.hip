@@ -397,6 +397,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows) return;
+    const float *src = ws_o + (int64_t)row * D + lane;
+    const int64_t split_stride = (int64_t)rows * D;
+    // the O_s of the first PRE splits are loaded together with the L_s (split
+    // index clamped into the workspace; splits past ns get weight 0), so that
+    // both arrive after one memory latency
+    constexpr int PRE = 8;
+    float pre[PRE][PER];
+#pragma unroll
+    for (int s = 0; s < PRE; ++s)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) pre[s][e] = src[min(s, ns - 1) * split_stride + 64 * e];
     const float ls = lane < ns ? ws_lse[(int64_t)lane * rows + row] : -INFINITY;
     float M = ls;
 #pragma unroll
@@ -408,10 +419,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     float acc[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    const float *src = ws_o + (int64_t)row * D + lane;
-    const int64_t split_stride = (int64_t)rows * D;
+#pragma unroll
+    for (int s = 0; s < PRE; ++s) {
+        const float ws = __shfl(w, s);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(ws, ws != 0.f ? pre[s][e] : 0.f, acc[e]);
+    }
 #pragma unroll 8
-    for (int s = 0; s < ns; ++s) {
+    for (int s = PRE; s < ns; ++s) {
         const float ws = __shfl(w, s);
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
