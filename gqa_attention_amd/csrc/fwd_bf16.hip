@@ -135,10 +135,16 @@ struct Ring {
 // One row tile: rows rb * BM .. of head group hg (sequence b), with the
 // workgroup's LDS (Ring<D, F8>::ELEMS bf16). Every thread of the workgroup
 // calls it; it issues no barrier before its first DMA, so the caller must
-// order it after any earlier use of the LDS.
+// order it after any earlier use of the LDS. With a counter `claim`, thread 0
+// adds 1 to it once the tile's first loads have landed (so that the atomic's
+// latency runs under the tile) and leaves the old value in `claimed`; the
+// return value says whether it did (not for a tile with no rows). Variable
+// length: cu_lds, if set, holds cu_seqlens_q then cu_seqlens_k (B + 1 each)
+// in LDS, read instead of global memory.
 template <int D, bool CAUSAL, bool VARLEN, bool F8>
-__device__ __forceinline__ void fwd_tile(const FwdParams &p, __bf16 *lds, const int hg, const int rb,
-                                         const int b) {
+__device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const int hg, const int rb,
+                                         const int b, unsigned int *claim, unsigned int &claimed,
+                                         const int *cu_lds = nullptr) {
     using CF = Cfg<D>;
     constexpr int NW = Waves<D>::NW, BM = Waves<D>::BM;
     constexpr int BN = CF::BN, C8 = CF::C8, NDMA = CF::NDMA;
@@ -183,7 +189,13 @@ __device__ __forceinline__ void fwd_tile(const FwdParams &p, __bf16 *lds, const 
     const int kvh = qh0 / p.G;
 
     int q_tok0, k_tok0, Lq, Lk;
-    if (VARLEN) {
+    if (VARLEN && cu_lds) {
+        const int *ck = cu_lds + p.B + 1;
+        q_tok0 = __builtin_amdgcn_readfirstlane(cu_lds[b]);
+        Lq = __builtin_amdgcn_readfirstlane(cu_lds[b + 1]) - q_tok0;
+        k_tok0 = __builtin_amdgcn_readfirstlane(ck[b]);
+        Lk = __builtin_amdgcn_readfirstlane(ck[b + 1]) - k_tok0;
+    } else if (VARLEN) {
         q_tok0 = p.cu_q[b];
         Lq = p.cu_q[b + 1] - q_tok0;
         k_tok0 = p.cu_k[b];
@@ -196,7 +208,8 @@ __device__ __forceinline__ void fwd_tile(const FwdParams &p, __bf16 *lds, const 
     }
     const int rows_total = Lq * p.gpack;
     const int row0 = rb * BM;
-    if (row0 >= rows_total) return;  // uniform over the workgroup
+    if (row0 >= rows_total) return false;  // uniform over the workgroup
+    bool did_claim = false;  // uniform
 
     const int shift = Lk - Lq;  // bottom-right causal alignment
     int kend = Lk;
@@ -596,6 +609,8 @@ __device__ __forceinline__ void fwd_tile(const FwdParams &p, __bf16 *lds, const 
             dma_v(3, vslot(I3{}));
             // Q, K(0), K(1), V(0) have landed (K(2) .. V(3) may not)
             asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (claim && tid == 0) claimed = atomicAdd(claim, 1u);
+            did_claim = claim != nullptr;
 #pragma unroll
             for (int s = 0; s < DSTEPS; ++s) qf[s] = *(const bf16x8 *)(Qs + wave * 32 * D + k_rd[s]);
             read_k(kslot(I0{}));
@@ -648,6 +663,8 @@ __device__ __forceinline__ void fwd_tile(const FwdParams &p, __bf16 *lds, const 
         dma_kv8(2, kslot(I2{}));
         dma_kv8(3, kslot(I3{}));
         barrier_keep2_f8();  // Q, KV(0), KV(1) have landed
+        if (claim && tid == 0) claimed = atomicAdd(claim, 1u);
+        did_claim = claim != nullptr;
         widen_v(kslot(I0{}), vslot(I0{}));
         const unsigned char *q8 = (const unsigned char *)Qs + wave * 32 * D;
 #pragma unroll
@@ -681,6 +698,8 @@ __device__ __forceinline__ void fwd_tile(const FwdParams &p, __bf16 *lds, const 
         dma_k(3, kslot(I3{}));
         dma_v(2, vslot(I2{}));
         barrier_keep2();  // Q, K(0), K(1), V(0) have landed
+        if (claim && tid == 0) claimed = atomicAdd(claim, 1u);
+        did_claim = claim != nullptr;
         // this lane's Q row, chunk 2 s + half (same offsets as the K reads)
 #pragma unroll
         for (int s = 0; s < DSTEPS; ++s) qf[s] = *(const bf16x8 *)(Qs + wave * 32 * D + k_rd[s]);
@@ -808,6 +827,7 @@ __device__ __forceinline__ void fwd_tile(const FwdParams &p, __bf16 *lds, const 
                                   : ((int64_t)b * p.Hq + head) * p.Sq + pos;
         p.lse[li] = lse;
     }
+    return did_claim;
 }
 
 // ---- Workgroup scheduling ----
@@ -829,19 +849,23 @@ __device__ __forceinline__ void fwd_tile(const FwdParams &p, __bf16 *lds, const 
 // each heaviest first, and workgroup w starts on list w mod 8 (its XCD under
 // round-robin dispatch, so that the tiles of one head group share that XCD's
 // L2). A tile is claimed by an atomic add on its list's counter p.sched[x]
-// (agent scope) after the previous tile ends (claiming one ahead did not
-// help: the tile's own in-order load waits then wait for the atomic too);
-// once its own list is empty a workgroup moves on to the next. p.sched[8]
+// (agent scope), issued during the previous tile once that tile's first
+// loads have landed (issued before them, the tile's in-order load waits would
+// wait for the atomic too); once its own list is empty a workgroup moves on
+// to the next. p.sched[8]
 // counts the workgroups that have finished; the last one returns the nine
 // counters to zero for the next launch that uses the same slot. The live row
 // tiles of every head group (ceil(G Lq / BM), none for an empty sequence) are
 // counted and prefix-summed per list in LDS at the start; with more than
-// kPersistMaxHg head groups every head group keeps n_rb entries and the empty
+// persist_max_hg<D> head groups every head group keeps n_rb entries and the empty
 // ones end at once. Fixed-length shapes keep one tile per workgroup: there,
 // persistent workgroups measured no faster (causal) or slower (the encoder,
 // whose equal tiles then start in lockstep).
 constexpr int kSchedSlots = 64;     // launches in flight per device that may share no slot
-constexpr int kPersistMaxHg = 1024;  // variable length: head groups the LDS prefix holds
+// Variable length: head groups the LDS prefix holds (d = 64: 512, so that
+// three workgroups still share a CU's LDS).
+template <int D>
+constexpr int persist_max_hg() { return D == 64 ? 512 : 1024; }
 __device__ unsigned int g_fwd_sched[kSchedSlots][16];  // zero at load; each launch leaves its slot at zero
 
 // Head group of entry j of list `list` (8 lists: the XCD order above).
@@ -866,8 +890,9 @@ fwd_bf16_kernel(FwdParams p) {
     __shared__ __attribute__((aligned(1024))) __bf16 lds[Ring<D, F8>::ELEMS];
     __shared__ long long s_work[kLptMax];
     __shared__ int s_order[kLptMax];           // sequence of longest-first rank r
-    __shared__ int s_pref[kPersistMaxHg + 8];  // per list: prefix of live row tiles
+    __shared__ int s_pref[persist_max_hg<D>() + 8];  // per list: prefix of live row tiles
     __shared__ int s_ctl[3];                   // claimed item, its list, lists not yet found empty
+    __shared__ int s_cu[2 * (kLptMax + 1)];    // cu_seqlens_q, cu_seqlens_k (B <= kLptMax)
     const int tid = threadIdx.x;
     if constexpr (!VARLEN) {
         // one row tile per workgroup
@@ -876,7 +901,9 @@ fwd_bf16_kernel(FwdParams p) {
         const int slot = xcd ? pid >> 3 : pid;
         const int j = slot / p.n_rb, rank = slot - j * p.n_rb;
         const int hg = hg_of<D, F8>(p, xcd ? pid & 7 : 0, j, xcd);
-        fwd_tile<D, CAUSAL, VARLEN, F8>(p, lds, hg, CAUSAL ? (p.n_rb - 1 - rank) : rank, hg / (p.Hq / p.gpack));
+        unsigned int unused = 0;
+        fwd_tile<D, CAUSAL, VARLEN, F8>(p, lds, hg, CAUSAL ? (p.n_rb - 1 - rank) : rank, hg / (p.Hq / p.gpack),
+                                        nullptr, unused);
         return;
     }
     const int mode = p.persist;
@@ -886,7 +913,11 @@ fwd_bf16_kernel(FwdParams p) {
     const bool lpt = VARLEN && p.B > 1 && p.B <= kLptMax;
     // dense lists of live row tiles (persistent, variable length); otherwise
     // every head group has n_rb entries and the empty ones end at once
-    const bool dense = VARLEN && mode != 0 && p.n_hg <= kPersistMaxHg;
+    const bool dense = VARLEN && mode != 0 && p.n_hg <= persist_max_hg<D>();
+    if (VARLEN && p.B <= kLptMax && tid <= p.B) {
+        s_cu[tid] = p.cu_q[tid];
+        s_cu[p.B + 1 + tid] = p.cu_k[tid];
+    }
     if (lpt) {
         if (tid < p.B) s_work[tid] = (long long)(p.cu_q[tid + 1] - p.cu_q[tid]) * (p.cu_k[tid + 1] - p.cu_k[tid]);
         __syncthreads();
@@ -944,7 +975,7 @@ fwd_bf16_kernel(FwdParams p) {
         const int nq = xq ? 8 : 1, per = q.n_hg / nq, hpq = q.Hq / q.gpack;
         const bool lq = VARLEN && q.B > 1 && q.B <= kLptMax;
         const bool pq = VARLEN && q.persist != 0;
-        const bool dq = pq && q.n_hg <= kPersistMaxHg;
+        const bool dq = pq && q.n_hg <= persist_max_hg<D>();
         auto n_items = [&](int l) {
             return dq ? __builtin_amdgcn_readfirstlane(s_pref[l * (per + 1) + per]) : per * q.n_rb;
         };
@@ -962,13 +993,16 @@ fwd_bf16_kernel(FwdParams p) {
         if (left == 0 || item >= n_items(list)) break;
         int j, rank, nrb = q.n_rb;
         if (dq) {
+            // j = the number of entries 1 .. per of the prefix that are <= item
+            // (pf[0] = 0 <= item < pf[per]), counted 64 at a time by ballot
             const int *pf = s_pref + list * (per + 1);
-            int lo = 0, hi = per;  // pf[lo] <= item < pf[hi]
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (__builtin_amdgcn_readfirstlane(pf[mid]) <= item) lo = mid; else hi = mid;
+            const int lane = tid & 63;
+            j = 0;
+            for (int j0 = 1; j0 <= per; j0 += 64) {
+                const int e = j0 + lane;
+                j += __builtin_popcountll(__builtin_amdgcn_ballot_w64(e <= per && pf[e] <= item));
             }
-            j = lo;
+            j = __builtin_amdgcn_readfirstlane(j);
             rank = item - __builtin_amdgcn_readfirstlane(pf[j]);
             nrb = __builtin_amdgcn_readfirstlane(pf[j + 1]) - (item - rank);
         } else {
@@ -978,10 +1012,14 @@ fwd_bf16_kernel(FwdParams p) {
         const int hg = hg_of<D, F8>(q, list, j, xq);
         const int r = hg / hpq;
         const int b = lq ? __builtin_amdgcn_readfirstlane(s_order[r]) : r;
-        fwd_tile<D, CAUSAL, VARLEN, F8>(q, lds, hg, CAUSAL ? (nrb - 1 - rank) : rank, b);
+        // the next tile of this list is claimed during this one
+        unsigned int nxt = 0;
+        const bool ahead = fwd_tile<D, CAUSAL, VARLEN, F8>(q, lds, hg, CAUSAL ? (nrb - 1 - rank) : rank, b,
+                                                           pq ? &q.sched[list] : nullptr, nxt,
+                                                           q.B <= kLptMax ? s_cu : nullptr);
         __syncthreads();  // the tile's use of the LDS has ended everywhere
         if (tid == 0) {
-            s_ctl[0] = pq ? (int)atomicAdd(&q.sched[list], 1u) : -1;
+            s_ctl[0] = !pq ? -1 : ahead ? (int)nxt : (int)atomicAdd(&q.sched[list], 1u);
             s_ctl[1] = list;
             s_ctl[2] = pq ? left : 0;
         }
