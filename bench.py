@@ -448,6 +448,82 @@ def split_sweep(torch, ga):
                       "median_best_over_picked": round(float(sorted(ratios)[len(ratios) // 2]), 4)}))
 
 
+def tile_timeline(torch, ga, gqa_inputs):
+    """Where a forward's time goes, per row tile, on the timeline probe build
+    (gqa_attention_amd/libgqa_attn_timeline.so: the library with per-tile
+    s_memrealtime stamps compiled in). For the encoder, prefill and packed
+    varlen workloads: after about 200 ms of back-to-back launches, one launch
+    records every row
+    tile's start, prologue end (its first K/V tiles and Q have landed and its
+    first scores are formed), loop end and end (output stores landed). Prints
+    a markdown table: per-tile prologue / loop / epilogue times, key-tile rate,
+    the CU time between consecutive tiles, the average number of tiles
+    resident per CU, and the idle tail."""
+    import ctypes
+    import numpy as np
+
+    ga._LIB_PATH = os.path.join(ROOT, "gqa_attention_amd", "libgqa_attn_timeline.so")
+    ga._lib = None
+    L = ga.lib()
+    L.gqa_attn_timeline_buffer.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    L.gqa_attn_timeline_buffer.restype = None
+    cap = 40000
+    buf = torch.zeros(8 * (cap + 1), dtype=torch.int64, device="cuda")
+    print("| workload | launch µs (not recording / recording) | tiles | prologue µs | loop µs | "
+          "ns per key tile | epilogue µs | µs between tiles on a CU | tiles resident per CU | "
+          "idle tail µs (mean / max) |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for w in (gqa_inputs.bert_base_encoder(), gqa_inputs.llama31_8b_prefill(),
+              gqa_inputs.varlen_packed_causal_48_12()):
+        q, k, v = w.q.cuda(), w.k.cuda(), w.v.cuda()
+        kw = dict(causal=w.causal, scale=w.scale)
+        if w.varlen:
+            kw.update(cu_seqlens_q=w.cu_seqlens_q.cuda(), cu_seqlens_k=w.cu_seqlens_k.cuda(),
+                      max_seqlen_q=w.max_seqlen_q, max_seqlen_k=w.max_seqlen_k)
+        plan = ga.FwdPlan(q, k, v, **kw)
+        plan.run()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        plan.run()
+        torch.cuda.synchronize()
+        # about 200 ms of back-to-back launches, so that the clocks have ramped
+        for _ in range(max(20, int(0.2 / max(time.perf_counter() - t, 1e-5)))):
+            plan.run()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
+        plan.run()
+        e[1].record()
+        buf.zero_()
+        L.gqa_attn_timeline_buffer(buf.data_ptr(), cap)
+        e[2].record()
+        plan.run()
+        e[3].record()
+        torch.cuda.synchronize()
+        L.gqa_attn_timeline_buffer(None, 0)
+        plain_us, rec_us = e[0].elapsed_time(e[1]) * 1e3, e[2].elapsed_time(e[3]) * 1e3
+        a = buf.cpu().numpy()
+        n = min(int(a[0]), cap)
+        r = a[8:8 + 8 * n].reshape(n, 8).astype(np.float64) / 100.0  # µs (100 MHz clock)
+        t0, t1, t2, t3 = r[:, 0], r[:, 1], r[:, 2], r[:, 3]
+        hw = a[8:8 + 8 * n].reshape(n, 8)[:, 4]
+        wg = a[8:8 + 8 * n].reshape(n, 8)[:, 6]
+        cu = (wg % 8) * 4096 + ((hw >> 8) & 0xFF)  # XCD (round-robin dispatch) + CU within it
+        gaps, tails, busy = [], [], 0.0
+        for c in np.unique(cu):
+            o = np.nonzero(cu == c)[0]
+            o = o[np.argsort(t0[o])]
+            busy += (t3[o] - t0[o]).sum()
+            g = t0[o[1:]] - t3[o[:-1]]
+            gaps.extend(g[g > 0].tolist())
+            tails.append(t3.max() - t3[o[-1]])
+        span = t3.max() - t0.min()
+        keyt = r[:, 5] * 100.0
+        print(f"| {w.name} | {plain_us:.1f} / {rec_us:.1f} | {n} | {np.mean(t1 - t0):.2f} | {np.mean(t2 - t1):.2f} | "
+              f"{np.sum(t2 - t1) / np.sum(keyt) * 1e3:.0f} | {np.mean(t3 - t2):.2f} | "
+              f"{np.mean(gaps) if gaps else 0.0:.2f} | {busy / len(np.unique(cu)) / span:.2f} | "
+              f"{np.mean(tails):.1f} / {np.max(tails):.1f} |", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -473,6 +549,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-counters", metavar="PMC_DIR",
                     help="write profiles/hbm_traffic.json from rocprofv3 counter runs and exit")
+    ap.add_argument("--tile-timeline", action="store_true",
+                    help="per-row-tile forward timeline on the probe build libgqa_attn_timeline.so "
+                         "(markdown table) and exit")
     ap.add_argument("--split-sweep", action="store_true",
                     help="time gqa_attn_decode at every split count over a grid of contiguous "
                          "bf16 caches, compare with gqa_attn_decode_num_splits (markdown table) "
@@ -501,6 +580,9 @@ def main():
 
     if args.split_sweep:
         split_sweep(torch, ga)
+        return
+    if args.tile_timeline:
+        tile_timeline(torch, ga, gqa_inputs)
         return
 
     # secondary workloads: warm up until the clocks have ramped, then time

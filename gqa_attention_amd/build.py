@@ -3,7 +3,9 @@
 Usage: python -m gqa_attention_amd.build [-v]
 
 Every library source under csrc/ is compiled to an object in parallel, then linked
-into ``gqa_attention_amd/libgqa_attn.so``; ``csrc/hbm_probe.hip`` becomes the
+into ``gqa_attention_amd/libgqa_attn.so`` (and ``libgqa_attn_timeline.so``, the
+same library with the forward's per-tile timestamps compiled in, a probe for
+``bench.py --tile-timeline``); ``csrc/hbm_probe.hip`` becomes the
 ``gqa_attention_amd/hbm_probe`` program (copy and read-stream reference
 kernels used to scale HBM byte counters) and ``csrc/issue_probe.hip`` the
 ``gqa_attention_amd/issue_probe`` program (whether the matrix cores run while
@@ -26,6 +28,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgqa_attn.so")
+TIMELINE_LIB = os.path.join(PKG, "libgqa_attn_timeline.so")  # probe build of the same library
 PROBE = os.path.join(PKG, "hbm_probe")  # copy / read-stream reference program
 PROBES = {"hbm_probe": ("hbm_probe.hip", []), "issue_probe": ("issue_probe.hip", []),
           "issue_probe_vform": ("issue_probe.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
@@ -49,10 +52,10 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, verbose: bool, extra=(), suffix: str = "") -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + suffix + ".o")
     lang = ["-x", "hip"]
-    cmd = [hipcc(), *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -68,16 +71,23 @@ def _compile(src: str, verbose: bool) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        futs = [ex.submit(_compile, s, verbose) for s in SOURCES]
+        # the timeline probe: the same library with the forward's per-tile
+        # timestamps compiled in (bench.py --tile-timeline)
+        tl_fut = ex.submit(_compile, "fwd_bf16.hip", verbose, ["-DGQA_TILE_TIMELINE=1"], "_timeline")
+        objs = [f.result() for f in futs]
+        tl_obj = tl_fut.result()
+    for out, members in ((LIB, objs), (TIMELINE_LIB, [tl_obj if o.endswith("fwd_bf16.o") else o
+                                                     for o in objs])):
+        tmp = out + ".tmp"
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *members]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link failed:\n{res.stderr}")
+        os.replace(tmp, out)
     for prog, (src, extra) in PROBES.items():
         out = os.path.join(PKG, prog)
         cmd = [hipcc(), *COMMON, *extra, os.path.join(CSRC, src), "-o", out + ".tmp"]

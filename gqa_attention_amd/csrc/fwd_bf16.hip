@@ -73,6 +73,12 @@ namespace {
 #ifndef GQA_PINGPONG
 #define GQA_PINGPONG 1
 #endif
+// Probe builds only (libgqa_attn_timeline.so, bench.py --tile-timeline):
+// every row tile appends its start, prologue end, loop end and end times
+// (s_memrealtime, 100 MHz) to the buffer set by gqa_attn_timeline_buffer.
+#ifndef GQA_TILE_TIMELINE
+#define GQA_TILE_TIMELINE 0
+#endif
 
 // Wavefronts per workgroup (32 query rows each): 8 at d = 128, where sharing
 // each K/V tile among 256 rows measured 3-5 % faster than 128 rows, 4 at
@@ -178,6 +184,8 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
     // live across them
     int tid = threadIdx.x;
     if constexpr (VARLEN) asm volatile("" : "+v"(tid));
+    [[maybe_unused]] unsigned long long tl0 = 0, tl1 = 0, tl2 = 0;
+    if constexpr (GQA_TILE_TIMELINE) tl0 = __builtin_amdgcn_s_memrealtime();
     // the wave index is wave-uniform: kept in a scalar register so that the
     // per-wave conditions below are scalar branches, not lane masks
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -624,6 +632,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
                 l_run += l_tile;
             }
             if (lag) data_barrier();  // group 1 starts one cluster behind
+            if constexpr (GQA_TILE_TIMELINE) tl1 = __builtin_amdgcn_s_memrealtime();
             int t = 0;
             for (; t + 4 < ntiles; t += 5) {
                 pp_step(I0{}, t);
@@ -772,6 +781,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
             barrier_tail(keep);
         }
     };
+    if constexpr (GQA_TILE_TIMELINE) tl1 = __builtin_amdgcn_s_memrealtime();
     int t = 0;
     for (; t + 3 < ntiles; t += 4) {
         step(I0{}, t, sa, sb);
@@ -786,6 +796,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
     // drain this wave's remaining (unused) DMA before the workgroup can end
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+    if constexpr (GQA_TILE_TIMELINE) tl2 = __builtin_amdgcn_s_memrealtime();
     // ---- epilogue: one division by l, L = m + log(l) ----
     const float l_tot = pair_sum32(l_run);
     const bool empty = !(l_tot > 0.f);
@@ -819,6 +830,27 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
             const int rp = rr / p.gpack;
             const int rh = qh0 + (rr - rp * p.gpack);
             *(u32x4 *)((__bf16 *)p.o + ((int64_t)(q_tok0 + rp) * p.Hq + rh) * D + c * 8) = v;
+        }
+    }
+    if constexpr (GQA_TILE_TIMELINE) {
+        // record: tile start, prologue end, loop end, end (stores landed),
+        // HW_ID, key tiles, workgroup; header word 0: count (p.split_chunk
+        // carries the capacity in records)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        unsigned long long *rec = reinterpret_cast<unsigned long long *>(p.ws_o);
+        if (tid == 0 && rec) {
+            const unsigned long long i = atomicAdd(rec, 1ull);
+            if (i < (unsigned long long)p.split_chunk) {
+                unsigned long long *r = rec + 8 * (1 + i);
+                r[0] = tl0;
+                r[1] = tl1;
+                r[2] = tl2;
+                r[3] = __builtin_amdgcn_s_memrealtime();
+                r[4] = (unsigned)__builtin_amdgcn_s_getreg((31 << 11) | 4);  // HW_ID
+                r[5] = (unsigned)ntiles;
+                r[6] = blockIdx.x;
+                r[7] = 1;
+            }
         }
     }
     if (row_ok && half == 0) {
@@ -1061,9 +1093,18 @@ unsigned int *sched_slot() {
     return base[dev] + 16 * (next[dev].fetch_add(1, std::memory_order_relaxed) % kSchedSlots);
 }
 
+#if GQA_TILE_TIMELINE
+void *g_timeline = nullptr;  // record buffer of the probe build
+int g_timeline_cap = 0;      // its capacity in records
+#endif
+
 template <int D, bool CAUSAL, bool VARLEN, bool F8>
 hipError_t launch_t(FwdParams p, hipStream_t s) {
     auto kernel = fwd_bf16_kernel<D, CAUSAL, VARLEN, F8>;
+#if GQA_TILE_TIMELINE
+    p.ws_o = static_cast<float *>(g_timeline);
+    p.split_chunk = g_timeline_cap;
+#endif
     long long grid = (long long)p.n_hg * p.n_rb;
     p.persist = 0;
     p.sched = nullptr;
@@ -1128,3 +1169,12 @@ hipError_t launch_fwd_fp8(const FwdParams &p, int d, bool causal, bool varlen, h
 }
 
 }  // namespace gqa
+
+#if GQA_TILE_TIMELINE
+// Probe build: device buffer of `capacity` 8-word records after an 8-word
+// header (word 0 counts the records written), or null to record nothing.
+extern "C" void gqa_attn_timeline_buffer(void *records, int capacity) {
+    gqa::g_timeline = records;
+    gqa::g_timeline_cap = capacity;
+}
+#endif
