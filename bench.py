@@ -282,7 +282,7 @@ def bench_decode_ex(torch, ga, wc, ns, steps, warmup, **warm):
     return dict(bytes=cache_kv_bytes(wc), wall=wall, avg_ms=avg_ms, steps=steps)
 
 
-def cpu_baseline(w, frac=0.25):
+def cpu_baseline(w, frac=0.5):
     """The fp64 oracle as it stands, run as a process pool (one worker per
     core this process may use, capped at 16, BLAS threads 1; oracle.pool) on
     a bounded sample of the same workload: the leading sequences (varlen) or
