@@ -378,6 +378,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
 
     const float c = p.scale_log2;
     float m_run = -INFINITY;  // reference max of scaled scores, log2 units
+    float m_neg = 0.f;        // -m_run, or 0 while m_run is -inf (no finite score yet)
     float l_run = 0.f;        // this lane's share of the running sum
     f32x16 oacc[DBLK];
 #pragma unroll
@@ -438,6 +439,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
         if (mxs > m_run) {
             const float alpha = fast_exp2(m_run - mxs);
             m_run = mxs;
+            m_neg = -mxs;
             l_run *= alpha;
 #pragma unroll
             for (int i = 0; i < DBLK; ++i)
@@ -448,17 +450,20 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
     // p = 2^(s c - m) in fp32, summed into l_tile and rounded to bf16 as the B
     // operand.
     auto probs = [&](const f32x16 (&sacc)[KB], bf16x8 (&pf)[KB][2], float &l_tile) {
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        // four partial sums, so that the adds do not form one serial chain
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
+        // four partial sums, so that the adds do not form one serial chain;
+        // each starts at its first value (no add of 0)
+        float part[4];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float pv = fast_exp2(fmaf(sacc[kb][8 * h2 + j], c, -m_use));
-                    part[j & 3] += pv;
+                    const float pv = fast_exp2(fmaf(sacc[kb][8 * h2 + j], c, m_neg));
+                    if (kb == 0 && h2 == 0 && j < 4)
+                        part[j] = pv;
+                    else
+                        part[j & 3] += pv;
                     pf[kb][h2][j] = (__bf16)pv;
                 }
         l_tile = (part[0] + part[1]) + (part[2] + part[3]);
