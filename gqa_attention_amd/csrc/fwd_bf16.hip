@@ -55,11 +55,17 @@
 #include <type_traits>
 
 #include "device_util.h"
+#include "fastdiv.h"
 #include "params.h"
 
 namespace gqa {
 
 namespace {
+
+// floor(n / d) for 0 <= n < 2^31 with (m, sh) = fastdiv_for(d) (fastdiv.h)
+__device__ __forceinline__ int fdiv(int n, unsigned int m, int sh) {
+    return m ? (int)(__umulhi((unsigned int)n, m) >> sh) : n;
+}
 
 #ifndef GQA_BN128
 #define GQA_BN128 32
@@ -191,10 +197,10 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, half = lane >> 5;
 
-    const int hpb = p.Hq / p.gpack;
-    const int seq_rank = hg / hpb;
+    const int hpb = p.hpb;
+    const int seq_rank = fdiv(hg, p.hpb_m, p.hpb_sh);
     const int qh0 = (hg - seq_rank * hpb) * p.gpack;
-    const int kvh = qh0 / p.G;
+    const int kvh = fdiv(qh0, p.g_m, p.g_sh);
 
     int q_tok0, k_tok0, Lq, Lk;
     if (VARLEN && cu_lds) {
@@ -223,14 +229,14 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
     int kend = Lk;
     if (CAUSAL) {
         const int last = min(row0 + BM, rows_total) - 1;
-        kend = min(Lk, last / p.gpack + 1 + shift);
+        kend = min(Lk, fdiv(last, p.gp_m, p.gp_sh) + 1 + shift);
     }
     const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
 
     // ---- this lane's query row ----
     const int rho = row0 + wave * 32 + col;
     const bool row_ok = rho < rows_total;
-    const int pos = rho / p.gpack;
+    const int pos = fdiv(rho, p.gp_m, p.gp_sh);
     const int head = qh0 + (rho - pos * p.gpack);
     const int row_kend = CAUSAL ? min(Lk, pos + 1 + shift) : Lk;
 
@@ -240,7 +246,32 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
     // limit is masked to -inf, so it adds nothing: p = 0 and no max moves.
     // Rows past the end hold clamped copies of the last row and are never
     // stored.
-    const int wave_kfull = CAUSAL ? min(Lk, (row0 + wave * 32) / p.gpack + 1 + shift) : Lk;
+    const int wave_kfull = CAUSAL ? min(Lk, fdiv(row0 + wave * 32, p.gp_m, p.gp_sh) + 1 + shift) : Lk;
+
+    // Packed rows rho = pos * gpack + h (h: head within the pack) that a lane
+    // loads or stores, rho0 + STEP i for i < N: f(i, pos, h, past) with past
+    // = the row lies beyond the last one (lpos, lh). One division for the
+    // first row, then exact increments (a division per row costs ~20 vector
+    // instructions).
+    const int gp = p.gpack;
+    const int rlast = rows_total - 1;
+    const int lpos = fdiv(rlast, p.gp_m, p.gp_sh), lh = rlast - lpos * gp;
+    auto for_rows = [&](int rho0, auto step_c, auto n_c, auto &&f) {
+        constexpr int STEP = decltype(step_c)::value, N = decltype(n_c)::value;
+        const int dpos = fdiv(STEP, p.gp_m, p.gp_sh), dh = STEP - dpos * gp;
+        int pos_i = fdiv(rho0, p.gp_m, p.gp_sh);
+        int h_i = rho0 - pos_i * gp;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            f(i, pos_i, h_i, rho0 + STEP * i > rlast);
+            pos_i += dpos;
+            h_i += dh;
+            if (h_i >= gp) {
+                h_i -= gp;
+                ++pos_i;
+            }
+        }
+    };
 
     // ---- Q fragment (B operand of S^T = K Q^T), kept in registers ----
     // It arrives through LDS: its direct loads are issued just before the
@@ -346,6 +377,27 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
             asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         else
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+
+    // Q rows of the tile into Qs by direct loads (load i of wave w fills bytes
+    // [1024 (w + NW i), +1024); lane l covers 16-byte chunk l % CQ of row
+    // (64 (w + NW i) + l) / CQ, swizzled as the K rows), rows past the end
+    // clamped to the last row (finite values whose results are never stored).
+    auto issue_q = [&] {
+        constexpr int QB = F8 ? 1 : 2;                      // bytes per Q element
+        constexpr int CQ = D * QB / 16;                     // 16-byte chunks per row
+        constexpr int NQL = BM * D * QB / 1024 / NW;        // loads per wave
+        const int r0 = (64 * wave + lane) / CQ;
+        const unsigned char *qbase = (const unsigned char *)p.q + ((int64_t)q_tok0 * p.Hq + qh0) * D * QB;
+        for_rows(row0 + r0, std::integral_constant<int, 64 * NW / CQ>{}, std::integral_constant<int, NQL>{},
+                 [&](int i, int pos_i, int h_i, bool past) {
+                     const int r = r0 + (64 * NW / CQ) * i;
+                     const int sw = F8 ? CF::swz8(r) : CF::swz_k(r);
+                     const unsigned char *src =
+                         qbase + ((int64_t)(past ? lpos : pos_i) * p.Hq + (past ? lh : h_i)) * D * QB +
+                         ((lane % CQ) ^ sw) * 16;
+                     lds_dma16(src, lds_addr(Qs) + 1024 * (wave + NW * i));
+                 });
     };
 
     // K operand (A of S^T = K Q^T): row kb*32 + col, chunk 2 s + half.
@@ -599,18 +651,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
         };
         using I4 = std::integral_constant<int, 4>;
         if (ntiles > 0) {
-            constexpr int NQ = BM * D * 2 / 1024 / NW;  // Q loads per wave
-#pragma unroll
-            for (int i = 0; i < NQ; ++i) {
-                const int idx = 64 * (wave + NW * i) + lane;
-                const int r = idx / C8;
-                const int rho = min(row0 + r, rows_total - 1);
-                const int qp = rho / p.gpack;
-                const int qh = qh0 + (rho - qp * p.gpack);
-                const __bf16 *src = (const __bf16 *)p.q + ((int64_t)(q_tok0 + qp) * p.Hq + qh) * D +
-                                    ((idx % C8) ^ CF::swz_k(r)) * 8;
-                lds_dma16(src, lds_addr(Qs) + 1024 * (wave + NW * i));
-            }
+            issue_q();
             dma_k(0, kslot(I0{}));
             dma_k(1, kslot(I1{}));
             dma_v(0, vslot(I0{}));
@@ -660,18 +701,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
     f32x16 sa[KB], sb[KB];
     if (ntiles > 0 && F8) {
         // fp8 Q rows (D bytes each, swizzled as the K rows), then KV(0..3)
-        constexpr int NQ8 = BM * D / 1024 / NW;  // Q loads per wave
-#pragma unroll
-        for (int i = 0; i < NQ8; ++i) {
-            const int idx = 64 * (wave + NW * i) + lane;
-            const int r = idx / C16;
-            const int rho = min(row0 + r, rows_total - 1);
-            const int qp = rho / p.gpack;
-            const int qh = qh0 + (rho - qp * p.gpack);
-            const unsigned char *src = (const unsigned char *)p.q + ((int64_t)(q_tok0 + qp) * p.Hq + qh) * D +
-                                       ((idx % C16) ^ CF::swz8(r)) * 16;
-            lds_dma16(src, lds_addr(Qs) + 1024 * (wave + NW * i));
-        }
+        issue_q();
         dma_kv8(0, kslot(I0{}));
         dma_kv8(1, kslot(I1{}));
         dma_kv8(2, kslot(I2{}));
@@ -692,18 +722,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
         raise_max(sa);
         barrier_lds();  // V(0) widened; K(0)'s slot is refilled with KV(4) in step 0
     } else if (ntiles > 0) {
-        constexpr int NQ = BM * D * 2 / 1024 / NW;  // Q loads per wave
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-            const int idx = 64 * (wave + NW * i) + lane;
-            const int r = idx / C8;
-            const int rho = min(row0 + r, rows_total - 1);
-            const int qp = rho / p.gpack;
-            const int qh = qh0 + (rho - qp * p.gpack);
-            const __bf16 *src = (const __bf16 *)p.q + ((int64_t)(q_tok0 + qp) * p.Hq + qh) * D +
-                                ((idx % C8) ^ CF::swz_k(r)) * 8;
-            lds_dma16(src, lds_addr(Qs) + 1024 * (wave + NW * i));
-        }
+        issue_q();
         dma_k(0, kslot(I0{}));
         dma_k(1, kslot(I1{}));
         dma_v(0, vslot(I0{}));
@@ -825,17 +844,16 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
             *(u32x2 *)(ow + col * D + c * 8 + 4 * half) = __builtin_bit_cast(u32x2, w);
         }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's writes precede its reads
-#pragma unroll
-    for (int j = 0; j < 32 * C8 / 64; ++j) {
-        const int idx = lane + 64 * j;
-        const int r = idx / C8, c = idx % C8;
-        const u32x4 v = *(const u32x4 *)(ow + r * D + ((c ^ (r & (C8 - 1))) * 8));
-        const int rr = row0 + wave * 32 + r;
-        if (rr < rows_total) {
-            const int rp = rr / p.gpack;
-            const int rh = qh0 + (rr - rp * p.gpack);
-            *(u32x4 *)((__bf16 *)p.o + ((int64_t)(q_tok0 + rp) * p.Hq + rh) * D + c * 8) = v;
-        }
+    {
+        // lane l stores 16-byte chunk l % C8 of rows l / C8 + (64 / C8) j
+        const int c = lane % C8, r0 = lane / C8;
+        __bf16 *obase = (__bf16 *)p.o + ((int64_t)q_tok0 * p.Hq + qh0) * D + c * 8;
+        for_rows(row0 + wave * 32 + r0, std::integral_constant<int, 64 / C8>{},
+                 std::integral_constant<int, 32 * C8 / 64>{}, [&](int j, int pos_j, int h_j, bool past) {
+                     const int r = r0 + (64 / C8) * j;
+                     const u32x4 v = *(const u32x4 *)(ow + r * D + ((c ^ (r & (C8 - 1))) * 8));
+                     if (!past) *(u32x4 *)(obase + ((int64_t)pos_j * p.Hq + h_j) * D) = v;
+                 });
     }
     if constexpr (GQA_TILE_TIMELINE) {
         // record: tile start, prologue end, loop end, end (stores landed),
@@ -936,10 +954,11 @@ fwd_bf16_kernel(FwdParams p) {
         const int pid = blockIdx.x;
         const bool xcd = (p.n_hg & 7) == 0;
         const int slot = xcd ? pid >> 3 : pid;
-        const int j = slot / p.n_rb, rank = slot - j * p.n_rb;
+        const int j = fdiv(slot, p.rb_m, p.rb_sh), rank = slot - j * p.n_rb;
         const int hg = hg_of<D, F8>(p, xcd ? pid & 7 : 0, j, xcd);
         unsigned int unused = 0;
-        fwd_tile<D, CAUSAL, VARLEN, F8>(p, lds, hg, CAUSAL ? (p.n_rb - 1 - rank) : rank, hg / (p.Hq / p.gpack),
+        fwd_tile<D, CAUSAL, VARLEN, F8>(p, lds, hg, CAUSAL ? (p.n_rb - 1 - rank) : rank,
+                                        fdiv(hg, p.hpb_m, p.hpb_sh),
                                         nullptr, unused);
         return;
     }
@@ -977,7 +996,7 @@ fwd_bf16_kernel(FwdParams p) {
                 const int j = j0 + lane;
                 int x = 0;
                 if (j < per_list) {
-                    const int r = hg_of<D, F8>(p, l, j, xcd) / (p.Hq / p.gpack);
+                    const int r = fdiv(hg_of<D, F8>(p, l, j, xcd), p.hpb_m, p.hpb_sh);
                     const int bb = lpt ? s_order[r] : r;
                     x = ((p.cu_q[bb + 1] - p.cu_q[bb]) * p.gpack + BM - 1) / BM;
                 }
@@ -1009,7 +1028,7 @@ fwd_bf16_kernel(FwdParams p) {
         asm volatile("" : "+s"(pp));
         const FwdParams &q = *(const FwdParams *)pp;
         const bool xq = (q.n_hg & 7) == 0;
-        const int nq = xq ? 8 : 1, per = q.n_hg / nq, hpq = q.Hq / q.gpack;
+        const int nq = xq ? 8 : 1, per = xq ? q.n_hg >> 3 : q.n_hg;
         const bool lq = VARLEN && q.B > 1 && q.B <= kLptMax;
         const bool pq = VARLEN && q.persist != 0;
         const bool dq = pq && q.n_hg <= persist_max_hg<D>();
@@ -1043,11 +1062,11 @@ fwd_bf16_kernel(FwdParams p) {
             rank = item - __builtin_amdgcn_readfirstlane(pf[j]);
             nrb = __builtin_amdgcn_readfirstlane(pf[j + 1]) - (item - rank);
         } else {
-            j = item / q.n_rb;
+            j = fdiv(item, q.rb_m, q.rb_sh);
             rank = item - j * q.n_rb;
         }
         const int hg = hg_of<D, F8>(q, list, j, xq);
-        const int r = hg / hpq;
+        const int r = fdiv(hg, q.hpb_m, q.hpb_sh);
         const int b = lq ? __builtin_amdgcn_readfirstlane(s_order[r]) : r;
         // the next tile of this list is claimed during this one
         unsigned int nxt = 0;
@@ -1111,6 +1130,13 @@ hipError_t launch_t(FwdParams p, hipStream_t s) {
     p.split_chunk = g_timeline_cap;
 #endif
     long long grid = (long long)p.n_hg * p.n_rb;
+    p.hpb = p.Hq / p.gpack;
+    const FastDiv fgp = fastdiv_for(p.gpack), fg = fastdiv_for(p.G), fh = fastdiv_for(p.hpb),
+                  frb = fastdiv_for(p.n_rb);
+    p.gp_m = fgp.m, p.gp_sh = fgp.sh;
+    p.g_m = fg.m, p.g_sh = fg.sh;
+    p.hpb_m = fh.m, p.hpb_sh = fh.sh;
+    p.rb_m = frb.m, p.rb_sh = frb.sh;
     p.persist = 0;
     p.sched = nullptr;
     if (VARLEN && persistent_enabled()) {

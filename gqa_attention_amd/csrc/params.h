@@ -35,6 +35,12 @@ struct FwdParams {
     // ints, zero on entry and on exit)
     int persist;
     unsigned int *sched;
+    // bf16 / fp8 kernels: divisions by launch constants as multiply-high and
+    // shift (fastdiv.h): by gpack, by G, by hpb = Hq / gpack (head groups per
+    // sequence) and by n_rb; set by the launcher
+    int hpb;
+    unsigned int gp_m, g_m, hpb_m, rb_m;
+    int gp_sh, g_sh, hpb_sh, rb_sh;
 };
 
 // One split-KV decode launch (bf16 queries; bf16 or fp8 e4m3 K/V cache).

@@ -7,7 +7,8 @@ lengths with empty and one-key caches and lengths around the 64-key split
 granularity, ragged batches of up to 256 sequences (scheduled longest first)
 and of more, sliding windows (one key, narrower and wider than the cache),
 fp8 e4m3 storage with dequantisation scales, MHA / GQA / MQA head ratios
-including groups of 16 and 24 query heads, and several split counts; plus
+including groups of 16 and 24 query heads, and several split counts (also
+over 1100 sequences, and repeated launches of interleaved shapes); plus
 exact identities: the contiguous full-length call equals ``gqa_attn_decode``
 bit for bit, a paged cache equals the same data stored contiguously, and
 out-of-range lengths are clamped.
@@ -134,6 +135,36 @@ def test_paged_equals_contiguous_bitwise(bs, fp8):
                           **args)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_split_merge_over_many_sequences():
+    """Split partials of 1100 sequences (8800 query rows, beyond the
+    longest-first ranking), empty and one-key caches among them, merged."""
+    lens = [(13 * i) % 97 for i in range(1100)]
+    w = gi.cache_decode(lens, 8, 8, 64, seed=12)
+    ro, rl = reference(w)
+    for ns in (2, 3):
+        o, l = run(w, num_splits=ns)
+        compare(o, l, ro, rl, torch.bfloat16, f"1100 sequences ns={ns}")
+
+
+def test_repeated_split_launches_agree():
+    """80 launches with splits, two shapes interleaved (one with empty
+    splits) through the same allocator: every repeat equals the first launch
+    of its shape bit for bit, and the first ones equal the oracle."""
+    wa = gi.cache_decode([0, 1, 40, 700, 2100], 32, 8, 128, seed=13)
+    wb = gi.cache_decode([300] * 6, 16, 2, 64, seed=14, with_seqlens=False)
+    first = {}
+    for i in range(80):
+        w, ns = (wa, 4) if i % 2 == 0 else (wb, 2 + (i // 2) % 2)
+        key = (i % 2, ns)
+        o, l = run(w, num_splits=ns)
+        if key not in first:
+            first[key] = (o, l)
+            ro, rl = reference(w)
+            compare(o, l, ro, rl, torch.bfloat16, f"reuse {key}")
+        else:
+            assert torch.equal(o, first[key][0]) and torch.equal(l, first[key][1]), (i, key)
 
 
 def test_lengths_out_of_range_are_clamped():
