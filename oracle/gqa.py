@@ -23,7 +23,7 @@ materialised and K/V expanded per query head:
   per-row statistic is L = m + log(l), the log of the row's sum of
   exponentials of the scaled scores (natural log).
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 
 * the scale multiplies Q Kᵀ before the softmax and the LSE is taken over the
   scaled scores;
