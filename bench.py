@@ -448,6 +448,37 @@ def split_sweep(torch, ga):
                       "median_best_over_picked": round(float(sorted(ratios)[len(ratios) // 2]), 4)}))
 
 
+def length_sweep(torch, ga, gqa_inputs):
+    """Forward (bf16 and fp8 inputs) and backward throughput against sequence
+    length: GQA 32 / 8 heads, max(1, 16384 / S) sequences of S tokens, N(0, 1)
+    inputs (e4m3 with q/k/v scales 0.5 / 0.25 / 0.5 for fp8), each entry
+    timed with HIP events over about 50 ms of back-to-back launches after a
+    50 ms warm-up. TFLOP/s of algorithmic work: 4 d per visible (query, key)
+    pair and query head for the forward, 10 d for the backward. Prints a
+    markdown table."""
+    rows = [(1024, True, 128), (4096, True, 128), (8192, True, 128), (32768, True, 128),
+            (1024, False, 128), (8192, False, 128), (32768, False, 128),
+            (1024, True, 64), (8192, True, 64), (32768, False, 64)]
+    warm = dict(warm_seconds=0.05, timed_seconds=0.05)
+    print("| S | causal | d | forward bf16 | forward fp8 | backward bf16 |")
+    print("|---|---|---|---|---|---|")
+    for i, (S, causal, d) in enumerate(rows):
+        B = max(1, 16384 // S)
+        w = gqa_inputs.fixed(B, 32, 8, S, S, d, seed=40 + i, causal=causal)
+        w8 = gqa_inputs.fixed_fp8(B, 32, 8, S, S, d, seed=60 + i, causal=causal, q_scale=0.5,
+                                  k_scale=0.25, v_scale=0.5)
+        tf = []
+        for wk in (w, w8):
+            r = bench_fwd(torch, ga, wk, 20, 5, 1, **warm)
+            tf.append(r["flops"] / (r["avg_ms"] * 1e-3) / 1e12)
+        r = bench_bwd(torch, ga, w, 10, 3, **warm)
+        tf.append(r["flops"] / (r["avg_ms"] * 1e-3) / 1e12)
+        print(f"| {S} | {'yes' if causal else 'no'} | {d} | {tf[0]:.0f} | {tf[1]:.0f} | {tf[2]:.0f} |",
+              flush=True)
+        del w, w8
+        torch.cuda.empty_cache()
+
+
 def tile_timeline(torch, ga, gqa_inputs):
     """Where a forward's time goes, per row tile, on the timeline probe build
     (gqa_attention_amd/libgqa_attn_timeline.so: the library with per-tile
@@ -552,6 +583,9 @@ def main():
     ap.add_argument("--tile-timeline", action="store_true",
                     help="per-row-tile forward timeline on the probe build libgqa_attn_timeline.so "
                          "(markdown table) and exit")
+    ap.add_argument("--length-sweep", action="store_true",
+                    help="forward (bf16, fp8) and backward TFLOP/s against sequence length "
+                         "(markdown table) and exit")
     ap.add_argument("--split-sweep", action="store_true",
                     help="time gqa_attn_decode at every split count over a grid of contiguous "
                          "bf16 caches, compare with gqa_attn_decode_num_splits (markdown table) "
@@ -583,6 +617,9 @@ def main():
         return
     if args.tile_timeline:
         tile_timeline(torch, ga, gqa_inputs)
+        return
+    if args.length_sweep:
+        length_sweep(torch, ga, gqa_inputs)
         return
 
     # secondary workloads: warm up until the clocks have ramped, then time
