@@ -26,8 +26,10 @@
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller. The library
- *    allocates nothing, keeps no mutable global state, never synchronises and
- *    never reads device data on the host.
+ *    calls no allocator; its only state is two static device arrays per GPU,
+ *    the variable-length forward's scheduling counters and the scratch of
+ *    gqa_attn_decode_noalloc (both described at those entry points). It
+ *    never synchronises and never reads device data on the host.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
  *    stream). Results are ready when the stream has reached the call.
  *  - Tensors are dense and contiguous with head_dim innermost. q, k, v, out
