@@ -17,6 +17,12 @@ the backward pass on the encoder, prefill and varlen workloads, and decode over
 general caches: ragged paged bf16 and fp8, sliding window; the fp8-input
 forward on the prefill and encoder shapes).
 
+Other modes (each prints its own table and exits): --workload W (any named
+workload as the main line), --pass backward, --split-sweep (decode split
+counts over a grid of caches), --length-sweep (forward and backward against
+sequence length), --tile-timeline (per-row-tile forward timeline on the probe
+build), --summarize-counters DIR (HBM bytes from rocprofv3 counter runs).
+
 Flop count: 4 * d per visible (query, key) pair per query head (two products,
 multiply-add = 2 flops); the backward counts 10 * d (five products). Decode bytes: the K and V cache bytes read,
 2 * B * Sk * Hkv * d * 2; for a general cache, the visible keys of every
