@@ -83,11 +83,13 @@ def source_digest(files) -> str:
     return h.hexdigest()[:16]
 
 
+_FWD_SOURCES = ["gqa_attention_amd/csrc/fwd_bf16.hip", "gqa_attention_amd/csrc/device_util.h",
+                "gqa_attention_amd/csrc/params.h", "gqa_attention_amd/csrc/fastdiv.h"]
 KERNEL_SOURCES = {
-    "fwd_bf16": ["gqa_attention_amd/csrc/fwd_bf16.hip", "gqa_attention_amd/csrc/device_util.h"],
-    "fwd_fp8": ["gqa_attention_amd/csrc/fwd_bf16.hip", "gqa_attention_amd/csrc/device_util.h"],
+    "fwd_bf16": _FWD_SOURCES,
+    "fwd_fp8": _FWD_SOURCES,
     "decode_bf16": ["gqa_attention_amd/csrc/decode_bf16.hip",
-                    "gqa_attention_amd/csrc/device_util.h"],
+                    "gqa_attention_amd/csrc/device_util.h", "gqa_attention_amd/csrc/params.h"],
 }
 
 
