@@ -79,6 +79,9 @@ __device__ __forceinline__ int fdiv(int n, unsigned int m, int sh) {
 #ifndef GQA_PINGPONG
 #define GQA_PINGPONG 1
 #endif
+#ifndef GQA_PP_VSPLIT
+#define GQA_PP_VSPLIT 2  // V^T operands of the next tile read in the matrix cluster (d = 128 ping-pong)
+#endif
 // Probe builds only (libgqa_attn_timeline.so, bench.py --tile-timeline):
 // every row tile appends its start, prologue end, loop end and end times
 // (s_memrealtime, 100 MHz) to the buffer set by gqa_attn_timeline_buffer.
@@ -522,13 +525,16 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
     };
     // O^T += V^T P^T. P^T key order in lane (col, half) for k-slot j:
     // key = kb*32 + 16*h2 + 8*(j/4) + 4*half + j%4, matched by the V^T reads.
-    auto load_v = [&](const __bf16 *vs, bf16x8 (&vf)[KB][2][DBLK]) {
+    // operands n0 <= n < n1 in (kb, h2, i) order (default: all)
+    auto load_v = [&](const __bf16 *vs, bf16x8 (&vf)[KB][2][DBLK], int n0 = 0, int n1 = 1 << 30) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                 for (int i = 0; i < DBLK; ++i) {
+                    const int n = (kb * 2 + h2) * DBLK + i;
+                    if (n < n0 || n >= n1) continue;
                     const __bf16 *vp = vs + (kb * 32 + 16 * h2) * D + v_rd[i];
                     const u32x2 lo = lds_read_tr16(vp);
                     const u32x2 hi = lds_read_tr16(vp + 8 * D);
@@ -567,25 +573,31 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
         // Waves w and w + 4 share a SIMD. Group 0 (waves 0-3) and group 1
         // (waves 4-7) run the same sequence of two clusters per K/V tile t:
         //   C(t): the LDS reads of K(t+1) (the A operand of S(t+1)), the
-        //         products O~ += V(t)^T P(t) while they arrive, then
+        //         products O~ += V(t)^T P(t) while they arrive, the
+        //         transposing reads of the first VSPLIT V(t+1)^T operands
+        //         (into registers those products have consumed), then
         //         S(t+1) = K(t+1) Q^T;
-        //   X(t): the DMA of K(t+5) and V(t+4), the probabilities
+        //   X(t): the DMA of K(t+5) and V(t+5), the probabilities
         //         P(t+1) = 2^(S(t+1) c - m) and their sum, and the transposing
-        //         LDS reads of V(t+1) for the next cluster,
+        //         LDS reads of the other V(t+1)^T operands for the next cluster,
         // with a workgroup barrier after each cluster. Group 1 passes one
         // barrier more at the start, so between two barriers one wave of each
         // SIMD issues matrix instructions while the other issues vector
         // instructions, and both issue LDS reads (a wave's LDS reads are
-        // served at a limited rate, so the reads are split between them).
+        // served at a limited rate, so the reads are split between them:
+        // 8 K + 2 VSPLIT transposing reads in C, 16 - 2 VSPLIT in X; moving
+        // 4 of the 16 into C measured 1-1.5 % faster).
         //
         // Ring safety (5 slots per tensor; barrier b ends interval b; group 0
         // runs C(t) in interval 2t+1 and X(t) in 2t+2, group 1 X(t-1) in 2t+1
         // and C(t) in 2t+2): K(j) is read in intervals 2j-1 and 2j, V(j) in
-        // 2j and 2j+1; the DMA of K(j+5) and V(j+5) into their slots is
-        // issued in X(j) and X(j+1) (intervals >= 2j+2). Each group waits at
-        // the end of X(t) for its loads issued in X(t-2) (vmcnt(4): the two
-        // latest groups of one K and one V load stay in flight), so K(j) has
-        // landed in both groups' shares by barrier 2j-3 and V(j) by 2j-1.
+        // 2j-1 .. 2j+1; the DMA of K(j+5) and V(j+5) into their slots is
+        // issued in X(j) (intervals >= 2j+2). Each group waits at the end of
+        // X(t) for its loads issued in X(t-2) (vmcnt(4): the two latest
+        // groups of one K and one V load stay in flight), so K(j) and V(j)
+        // have landed in both groups' shares by barrier 2j-3; the prologue
+        // issues K(0..4) and V(0..4) and waits for K(1) and V(1), which group
+        // 0's first C cluster reads.
         const bool lag = wave >= NW / 2;  // wave-uniform
         bf16x8 kf[DSTEPS];                // K(t+1), the A operand of S(t+1)
         bf16x8 vfr[KB][2][DBLK];          // V(t)^T operand
@@ -614,12 +626,16 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
             asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
         };
+        constexpr int VSPLIT = GQA_PP_VSPLIT;  // V^T(t+1) operands read in C(t) instead of X(t)
         auto cluster_c = [&](auto jc, int t) {
             constexpr int J = decltype(jc)::value;
             __builtin_amdgcn_s_setprio(2);
             const bool more = t + 1 < ntiles;  // wave-uniform
             if (more) read_k(kslot(std::integral_constant<int, J + 1>{}));
             accumulate(vfr, pfr);
+            if constexpr (VSPLIT > 0) {
+                if (more) load_v(vslot(std::integral_constant<int, J + 1>{}), vfr, 0, VSPLIT);
+            }
             if (more) score_products();
             __builtin_amdgcn_s_setprio(0);
         };
@@ -627,10 +643,13 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
             constexpr int J = decltype(jc)::value;
             if (t + 1 < ntiles) {
                 dma_k(t + 5, kslot(std::integral_constant<int, J + 5>{}));
-                dma_v(t + 4, vslot(std::integral_constant<int, J + 4>{}));
+                if constexpr (VSPLIT > 0)
+                    dma_v(t + 5, vslot(std::integral_constant<int, J + 5>{}));
+                else
+                    dma_v(t + 4, vslot(std::integral_constant<int, J + 4>{}));
                 mask(t + 1, sc);
                 float l_tile;
-                load_v(vslot(std::integral_constant<int, J + 1>{}), vfr);
+                load_v(vslot(std::integral_constant<int, J + 1>{}), vfr, VSPLIT);
                 probs(sc, pfr, l_tile);
                 if (__builtin_amdgcn_ballot_w64(l_tile > kTileSumBound)) {
                     raise_max(sc);
@@ -661,8 +680,15 @@ __device__ __forceinline__ bool fwd_tile(const FwdParams &p, __bf16 *lds, const 
             dma_v(2, vslot(I2{}));
             dma_k(4, kslot(I4{}));
             dma_v(3, vslot(I3{}));
-            // Q, K(0), K(1), V(0) have landed (K(2) .. V(3) may not)
-            asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if constexpr (VSPLIT > 0) {
+                dma_v(4, vslot(I4{}));
+                // Q, K(0), K(1), V(0), K(2), V(1) have landed (K(3) .. V(4)
+                // may not): group 0's first C cluster reads part of V(1)
+                asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            } else {
+                // Q, K(0), K(1), V(0) have landed (K(2) .. V(3) may not)
+                asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            }
             if (claim && tid == 0) claimed = atomicAdd(claim, 1u);
             did_claim = claim != nullptr;
 #pragma unroll
