@@ -35,6 +35,18 @@ namespace {
 #define GQA_DEC_WPE 2  // waves per SIMD the register budget is sized for
 #endif
 
+// K/V cache loads. Every cache byte is read once per call; on bf16 caches the
+// non-temporal hint measured 1.5-3 % faster (B 64 x 4096 keys, 32/8 heads,
+// d 128, 1-8 splits; ragged paged caches +1.8 %), on fp8 caches 2 % slower,
+// so it is used for bf16 only.
+template <typename T, bool NT>
+__device__ __forceinline__ T load_kv(const unsigned char *ptr) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load((const T *)ptr);
+    else
+        return *(const T *)ptr;
+}
+
 constexpr int NTHREADS = 256;
 constexpr int NWAVES = 4;
 constexpr int TK = 32;        // keys per wave tile
@@ -189,19 +201,19 @@ decode_bf16_kernel(DecodeParams p) {
                 // the lane's 8 NS codes are contiguous: 16-byte loads
 #pragma unroll
                 for (int h = 0; h < NS / 2; ++h) {
-                    const u32x4 w = *(const u32x4 *)(krow + 16 * h);
+                    const u32x4 w = load_kv<u32x4, !FP8>(krow + 16 * h);
                     kd[kt][2 * h] = kraw_t{w[0], w[1]};
                     kd[kt][2 * h + 1] = kraw_t{w[2], w[3]};
                 }
             } else {
 #pragma unroll
-                for (int s = 0; s < NS; ++s) kd[kt][s] = *(const kraw_t *)(krow + 32 * s * ESZ);
+                for (int s = 0; s < NS; ++s) kd[kt][s] = load_kv<kraw_t, !FP8>(krow + 32 * s * ESZ);
             }
         }
 #pragma unroll
         for (int i = 0; i < NVL; ++i) {
             const int key = min(t0 + lane / VCPR + i * (64 / VCPR), w_hi - 1);
-            vd[i] = *(const u32x4 *)key_ptr(vbase, key);
+            vd[i] = load_kv<u32x4, !FP8>(key_ptr(vbase, key));
         }
     };
     auto k_operand = [&](const kraw_t &raw) -> bf16x8 {
