@@ -48,6 +48,7 @@ constexpr int NW = 4;  // wavefronts per workgroup
 constexpr int NTHREADS = 64 * NW;
 constexpr int NSLOT = 3;  // LDS ring depth (tiles two ahead)
 
+
 // 16-byte chunk slot of chunk c in row r: c ^ swz(r). d = 128 (16 chunks a
 // row): 16 consecutive rows read at one chunk hit 16 distinct slots, and the
 // 4-row x 2-chunk footprint of a transposing read also hits distinct slots.
@@ -73,8 +74,12 @@ __device__ __forceinline__ void wait_barrier() {
         asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else if constexpr (N == 5)
         asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (N == 6)
+        asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (N == 10)
+        asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else
-        static_assert(N <= 5, "wait count");
+        static_assert(N <= 6 || N == 10, "wait count");
 }
 
 // Start of head group hgl of sequence b in a workspace array (rows padded to
@@ -143,7 +148,12 @@ bwd_dkdv_kernel(BwdParams p) {
     // the two 64-VGPR accumulators), and a 2-slot ring keeps two workgroups
     // per CU; d = 64: V in registers, 3-slot ring.
     constexpr bool VLDS = D == 128 && !ONE;
-    constexpr int NS = VLDS ? 2 : NSLOT;
+    // PIPE (ONE): the scores of row tile t + 1 are formed while tile t's
+    // probabilities are, so the single wave's matrix core runs under its own
+    // exponentials; the ring then holds tile t - 1's slot for the next DMA,
+    // tiles t and t + 1 being read, and tile t + 2 in flight (4 slots).
+    constexpr bool PIPE = ONE;
+    constexpr int NS = VLDS ? 2 : PIPE ? 4 : NSLOT;
     __shared__ __attribute__((aligned(1024))) unsigned char ring[NS * SLOT];
     __shared__ __attribute__((aligned(16))) __bf16 vlds[VLDS ? NW * 32 * D : 8];
 
@@ -295,7 +305,9 @@ bwd_dkdv_kernel(BwdParams p) {
                 ++dpos[i];
             }
         }
-        const int r8 = t * BR + 8 * wave + 4 * (lane & 1);
+        // tiles past the last one (issued so that every step has the same
+        // loads) re-read the last tile's L and D
+        const int r8 = min(t, t_hi - 1) * BR + 8 * wave + 4 * (lane & 1);
         const float *src = (lane & 2) ? d_src + r8 : l_src + r8;
         if (lane < 4) lds_dma16_u(src, lds_addr(base + 2 * TILE * 2) + 64 * wave_u);
     };
@@ -335,6 +347,102 @@ bwd_dkdv_kernel(BwdParams p) {
         return (t * BR) / G + shift >= wk1;
     };
 
+    if constexpr (PIPE) {
+        // S = Q K^T and dP = dO V^T of the tile in ring slot bs (rows 8 (j/4)
+        // + 4 half + j%4, key col)
+        auto scores = [&](const unsigned char *bs, int rs, f32x16 &sa, f32x16 &da) {
+            const __bf16 *q_ = (const __bf16 *)bs;
+            const __bf16 *g_ = (const __bf16 *)(bs + TILE * 2);
+            bf16x8 qa[DSTEPS], ga[DSTEPS];
+#pragma unroll
+            for (int s = 0; s < DSTEPS; ++s) {
+                qa[s] = *(const bf16x8 *)(q_ + (rs ^ (16 * s)));
+                ga[s] = *(const bf16x8 *)(g_ + (rs ^ (16 * s)));
+            }
+            sa = f32x16{};
+            da = f32x16{};
+#pragma unroll
+            for (int s = 0; s < DSTEPS; ++s) sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[s], sa, 0, 0, 0);
+#pragma unroll
+            for (int s = 0; s < DSTEPS; ++s) da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[s], vf[s], da, 0, 0, 0);
+        };
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+        if (t_lo < t_hi) {
+            for (int j = 0; j < NS - 1; ++j) dma_tile(t_lo + j, j);
+            wait_barrier<(NS - 2) * NLOAD>();  // tile t_lo has landed
+            int rs_b = rs0;
+            asm volatile("" : "+v"(rs_b));
+            scores(ring, rs_b, sacc, dpacc);
+        }
+        for (int t = t_lo; t < t_hi; ++t) {
+            const int it = t - t_lo;
+            // tile t + 1 has landed (tile t + 2 may not); every wave is done
+            // with tile t - 1, whose slot the next DMA fills
+            wait_barrier<(NS - 3) * NLOAD>();
+            dma_tile(t + NS - 1, it + NS - 1);
+            const unsigned char *base = ring + (it % NS) * SLOT;
+            const unsigned char *nbase = ring + ((it + 1) % NS) * SLOT;
+            int rs_b = rs0, tr_b = tr0;
+            asm volatile("" : "+v"(rs_b), "+v"(tr_b));  // keep the derived offsets in the loop
+            const __bf16 *qt = (const __bf16 *)base;
+            const __bf16 *gt = (const __bf16 *)(base + TILE * 2);
+            const float *misc = (const float *)(base + 2 * TILE * 2);
+            bf16x8 tg[2][DBLK], tq[2][DBLK];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < DBLK; ++i) {
+                    const int tri = tr_b ^ (32 * i);
+                    const int o = 16 * h2 * D + tri, o8 = 16 * h2 * D + (tri ^ 16) + 8 * D;
+                    const u32x2 g0 = lds_read_tr16(gt + o), g1 = lds_read_tr16(gt + o8);
+                    const u32x2 q0 = lds_read_tr16(qt + o), q1 = lds_read_tr16(qt + o8);
+                    tg[h2][i] = __builtin_bit_cast(bf16x8, u32x4{g0[0], g0[1], g1[0], g1[1]});
+                    tq[h2][i] = __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]});
+                }
+            float pv[16], dsv[16];
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+                const f32x4 lv = *(const f32x4 *)(misc + 16 * blk + 4 * half);
+                const f32x4 dv4 = *(const f32x4 *)(misc + 16 * blk + 8 + 4 * half);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 4 * blk + e;
+                    pv[j] = fast_exp2(fmaf(sacc[j], c, -lv[e]));
+                    dsv[j] = pv[j] * (dpacc[j] - dv4[e]);
+                }
+            }
+            // the next tile's scores (the last step scores the re-loaded
+            // tile past the end, which has landed too, and drops them)
+            f32x16 sacc_n, dpacc_n;
+            scores(nbase, rs_b, sacc_n, dpacc_n);
+            if (!tile_full(t)) {
+                // rows past the end carry arbitrary L and D: select, not scale
+                const int rho0 = t * BR + 4 * half;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int rho = rho0 + 8 * (j >> 2) + (j & 3);
+                    const bool vis = rho < rows_total && (!CAUSAL || rho >= row_min);
+                    pv[j] = vis ? pv[j] : 0.f;
+                    dsv[j] = vis ? dsv[j] : 0.f;
+                }
+            }
+            bf16x8 pf[2], dsf[2];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                pf[j >> 3][j & 7] = (__bf16)pv[j];
+                dsf[j >> 3][j & 7] = (__bf16)dsv[j];
+            }
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int i = 0; i < DBLK; ++i) {
+                    dvacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tg[h2][i], pf[h2], dvacc[i], 0, 0, 0);
+                    dkacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[h2][i], dsf[h2], dkacc[i], 0, 0, 0);
+                }
+            sacc = sacc_n;
+            dpacc = dpacc_n;
+        }
+    } else {
     // NS - 1 tiles in flight ahead of the one being computed.
     if (t_lo < t_hi)
         for (int j = 0; j < NS - 1; ++j) dma_tile(t_lo + j, j);
@@ -463,6 +571,7 @@ bwd_dkdv_kernel(BwdParams p) {
                 dvacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pf[h2], dvacc[i], 0, 0, 0);
                 dkacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsf[h2], dkacc[i], 0, 0, 0);
             }
+    }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the (unused) tail loads
 
