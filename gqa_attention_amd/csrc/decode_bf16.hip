@@ -35,10 +35,13 @@ namespace {
 #define GQA_DEC_WPE 2  // waves per SIMD the register budget is sized for
 #endif
 
-// K/V cache loads. Every cache byte is read once per call; on bf16 caches the
-// non-temporal hint measured 1.5-3 % faster (B 64 x 4096 keys, 32/8 heads,
-// d 128, 1-8 splits; ragged paged caches +1.8 %), on fp8 caches 2 % slower,
-// so it is used for bf16 only.
+// K/V cache loads. Every cache byte is read once per call. V rows (whole
+// 16-byte chunks of each row, 16 lanes per bf16 row) carry the non-temporal
+// hint; K loads keep the default policy. Measured on B 64 x 4096 keys, 32/8
+// heads, d 128 against the hint on both: ns 1 / 2 / 4 / 8 at 6.31 / 6.04 /
+// 5.96 / 6.07 TB/s instead of 5.85 / 5.66 / 5.64 / 5.65; on the ragged paged
+// fp8 cache the hint on V alone gives +11-13 % over no hint and the hint on
+// K costs 4 %.
 template <typename T, bool NT>
 __device__ __forceinline__ T load_kv(const unsigned char *ptr) {
     if constexpr (NT)
@@ -201,19 +204,19 @@ decode_bf16_kernel(DecodeParams p) {
                 // the lane's 8 NS codes are contiguous: 16-byte loads
 #pragma unroll
                 for (int h = 0; h < NS / 2; ++h) {
-                    const u32x4 w = load_kv<u32x4, !FP8>(krow + 16 * h);
+                    const u32x4 w = load_kv<u32x4, false>(krow + 16 * h);
                     kd[kt][2 * h] = kraw_t{w[0], w[1]};
                     kd[kt][2 * h + 1] = kraw_t{w[2], w[3]};
                 }
             } else {
 #pragma unroll
-                for (int s = 0; s < NS; ++s) kd[kt][s] = load_kv<kraw_t, !FP8>(krow + 32 * s * ESZ);
+                for (int s = 0; s < NS; ++s) kd[kt][s] = load_kv<kraw_t, false>(krow + 32 * s * ESZ);
             }
         }
 #pragma unroll
         for (int i = 0; i < NVL; ++i) {
             const int key = min(t0 + lane / VCPR + i * (64 / VCPR), w_hi - 1);
-            vd[i] = load_kv<u32x4, !FP8>(key_ptr(vbase, key));
+            vd[i] = load_kv<u32x4, true>(key_ptr(vbase, key));
         }
     };
     auto k_operand = [&](const kraw_t &raw) -> bf16x8 {
