@@ -284,9 +284,10 @@ int gqa_attn_decode_ex(const void *q, const void *k_cache, const void *v_cache, 
  * range (max_seqlen_k, or window_left + 1 when smaller). On a split-count
  * sweep of contiguous bf16 caches with 32 query and 8 K/V heads (B 1..128,
  * 512..32768 keys, d 64 and 128; 64 points) the pick is the fastest count at
- * 41 points, its time is the best count's at the median and at most 1.19
- * times it; the largest losses are on long caches at large B, where 8 or 16
- * splits run 7-15 % faster than the 1 picked.
+ * 40 points, its time is the best count's at the median and at most 1.29
+ * times it; the largest losses are on short calls (8-20 us: B <= 4 at 2048
+ * keys), where 8 or 16 splits beat the picked 4, and on long caches at
+ * large B at d 64, where 16 splits run 15-17 % faster than the 1 picked.
  * Returns 0 for invalid arguments (same rules as gqa_attn_decode_ex).
  */
 int gqa_attn_decode_num_splits(int B, int Hq, int Hkv, int d, int max_seqlen_k, int window_left,
